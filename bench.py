@@ -1,0 +1,300 @@
+"""Benchmark of the MI355X Muon / Dimuon optimizer step.
+
+One step = one pass of the whole hot path (momentum, conditioning, Frobenius
+normalisation, Newton-Schulz iterations, post-scale, weight update) over one
+batch of matrices whose inputs are already resident in HBM.
+
+Default workload: the LoRA batch (64 pairs of 8 x 4096 and 4096 x 8, fp32
+master weights, Dimuon).  Its 84 MB per step would fit the 256 MB Infinity
+Cache, so four independent buffer sets are rotated.  The GPT-2, square
+4096^2 and MoE batches are measured as well and reported under
+"workloads".
+
+Prints one JSON line.  Rank 0 only; one GPU (`--gpus` above 1 is refused).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--variant", default=None, choices=[None, "muon", "dimuon"])
+    ap.add_argument("--extra", default="c3:muon,c4:dimuon,c4:muon,c5:dimuon",
+                    help="comma list of config:variant measured besides the main one, or 'none'")
+    ap.add_argument("--extra-steps", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=0, help="buffer sets rotated (0: automatic)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def make_workload(name, device, variant=None):
+    import workloads as W
+    if name == "c1":
+        wl = W.lora_toy(seed=0, device=device)
+    elif name == "c2":
+        wl = W.lora_batch(device=device)
+    elif name == "c3":
+        wl = W.gpt2_hidden(device=device)
+    elif name == "c4":
+        wl = W.square_batch(device=device, variant=variant or "dimuon")
+    else:
+        wl = W.moe_experts(device=device)
+    if variant:
+        wl.variant = variant
+    return wl
+
+
+def algorithmic(wl, is_thin):
+    """Per-step algorithmic work: bytes of the thin path, NS flops of the MFMA path."""
+    size = {"f32": 4, "bf16": 2}
+    per_elem = size[wl.g_dtype] + 2 * size[wl.mom_dtype] + 2 * size[wl.w_dtype]
+    thin_bytes = gram = poly = comb = 0
+    for m in wl.mats:
+        rows, cols = m.shape
+        k, n = min(rows, cols), max(rows, cols)
+        if is_thin(rows, cols):
+            thin_bytes += rows * cols * per_elem
+        else:
+            gram += k * k * n
+            poly += k ** 3
+            comb += 2 * k * k * n
+    return {"thin_bytes": thin_bytes, "gram_flops": gram, "poly_flops": poly, "comb_flops": comb,
+            "hbm_bytes_min": sum(m.shape[0] * m.shape[1] for m in wl.mats) * per_elem}
+
+
+def is_thin(m, n):
+    k, big = min(m, n), max(m, n)
+    p = 1
+    while p < k:
+        p *= 2
+    return k <= 32 and p * big <= 32768
+
+
+def measure(wl, steps, warmup, sets, ns_dtype=None):
+    import torch
+    import dimuon_newton_schulz_amd as D
+
+    cfg = D.StepConfig(lr=wl.lr, momentum=wl.mu, ns_steps=wl.ns_steps, w_dtype=wl.w_dtype,
+                       g_dtype=wl.g_dtype, mom_dtype=wl.mom_dtype, ns_dtype=ns_dtype or wl.ns_dtype)
+    step_fn = D.dimuon_step if wl.variant == "dimuon" else D.muon_step
+    batches = []
+    for s in range(sets):
+        params = [D.Param(w=m.w.clone() if s else m.w, g=m.g.clone() if s else m.g,
+                          mom=m.m_prev.clone() if s else m.m_prev) for m in wl.mats]
+        batches.append((params, D.workspace_for(params, cfg)))
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        p, ws = batches[i % sets]
+        step_fn(p, cfg, workspace=ws)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, HIP events around it on the library's stream.
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        p, ws = batches[i % sets]
+        step_fn(p, cfg, workspace=ws)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+
+    # Same K steps again with one HIP event after every kernel launch (the
+    # library's launch-event hook), for per-kernel durations.
+    lib = D.load_library()
+    per_step = 64
+    n_ev = per_step * steps
+    import ctypes
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    for e in events:
+        e.record()
+    torch.cuda.synchronize()
+    handles = (ctypes.c_void_p * n_ev)(*[e.cuda_event for e in events])
+    kinds = (ctypes.c_int32 * n_ev)()
+    counts = []
+    hs = ctypes.sizeof(ctypes.c_void_p)
+    for i in range(steps):
+        p, ws = batches[i % sets]
+        base = i * per_step
+        lib.muon_set_launch_events(ctypes.cast(ctypes.addressof(handles) + base * hs, ctypes.c_void_p),
+                                   ctypes.cast(ctypes.addressof(kinds) + base * 4,
+                                               ctypes.POINTER(ctypes.c_int32)), per_step)
+        step_fn(p, cfg, workspace=ws)
+        counts.append(lib.muon_set_launch_events(None, None, 0))
+    torch.cuda.synchronize()
+    per_kind = {}
+    for i in range(steps):
+        base = i * per_step
+        for j in range(1, counts[i]):
+            kind = D.LAUNCH_KINDS[kinds[base + j]]
+            dt = events[base + j - 1].elapsed_time(events[base + j])
+            tot, n = per_kind.get(kind, (0.0, 0))
+            per_kind[kind] = (tot + dt, n + 1)
+    del batches
+    torch.cuda.empty_cache()
+    return cfg, ms, per_kind
+
+
+def roofline_for(wl, cfg, per_kind, work, steps):
+    """Dominant kernel (largest total time) and its achieved rate."""
+    kind = max(per_kind, key=lambda k: per_kind[k][0])
+    tot_ms, launches = per_kind[kind]
+    avg_ms = tot_ms / launches
+    per_launch_iters = 1
+    if kind == "thin":
+        achieved = work["thin_bytes"] / (avg_ms * 1e-3) / 1e9
+        return kind, {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                      "kernel": "k_thin", "avg_launch_ms": round(avg_ms, 5),
+                      "bytes_per_launch": work["thin_bytes"]}
+    flops = {"combine": work["comb_flops"], "gram": work["gram_flops"], "poly": work["poly_flops"]}.get(kind)
+    if flops is None:
+        # a streaming kernel dominates: report bytes of one pass
+        achieved = work["hbm_bytes_min"] / (avg_ms * 1e-3) / 1e9
+        return kind, {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": kind,
+                      "avg_launch_ms": round(avg_ms, 5)}
+    peak = PEAK_TFLOPS[cfg.ns_dtype]
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    names = {"combine": "k_combine_bf16", "gram": "k_syrk_bf16", "poly": "k_syrk_bf16"}
+    return kind, {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                  "frac": round(achieved / peak, 4), "traffic": None,
+                  "kernel": names[kind] if cfg.ns_dtype == "bf16" else names[kind].replace("bf16", "f32"),
+                  "avg_launch_ms": round(avg_ms, 5), "flops_per_launch": flops}
+
+
+def host_sample(name, variant):
+    """Host copy of a representative slice of the workload for the oracle:
+    the whole batch when it is small, otherwise one matrix of each shape."""
+    import workloads as W
+    if name == "c1":
+        wl = W.lora_toy(seed=0)
+    elif name == "c2":
+        wl = W.lora_batch()
+    elif name == "c3":
+        wl = W.gpt2_hidden(layers=1)
+    elif name == "c4":
+        wl = W.square_batch(count=1)
+    else:
+        wl = W.moe_experts(experts=1)
+    wl.variant = variant
+    return wl
+
+
+def cpu_baseline(wl_host, full_count, seconds):
+    """The oracle as it stands, on host cores, over a bounded sample of the batch."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    fn = O.dimuon_step if wl_host.variant == "dimuon" else O.muon_step
+    mats = [(m.w.double().numpy(), m.g.double().numpy(), m.m_prev.double().numpy()) for m in wl_host.mats]
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        w, g, mp = mats[done % len(mats)]
+        fn(w, g, mp, lr=wl_host.lr, mu=wl_host.mu, mom_dtype=wl_host.mom_dtype, w_dtype=wl_host.w_dtype)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds and done % len(mats) == 0:
+            break
+    per_matrix = el / done
+    steps_per_s = 1.0 / (per_matrix * full_count)
+    return {"value": round(steps_per_s, 6), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} matrix steps over {len(mats)} distinct matrices of the batch in {el:.1f} s "
+                      f"(float64 numpy); steps/s = 1 / (mean seconds per matrix x {full_count} matrices)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
+              f"(matrices are independent and would shard by ownership across GPUs)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import dimuon_newton_schulz_amd as D
+
+    D.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    variant = args.variant or ("muon" if args.config == "c3" else "dimuon")
+    wl = make_workload(args.config, dev, variant)
+    work = algorithmic(wl, is_thin)
+    full_count = wl.count
+    sets = args.sets or (4 if work["hbm_bytes_min"] < 300e6 else 1)
+    cfg, ms, per_kind = measure(wl, args.steps, args.warmup, sets)
+    kind, roof = roofline_for(wl, cfg, per_kind, work, args.steps)
+    total_flops = 5 * (work["gram_flops"] + work["poly_flops"] + work["comb_flops"])
+    dtype = "f32" if (wl.w_dtype == "f32" and all(is_thin(*m.shape) for m in wl.mats)) else cfg.ns_dtype
+    out = {
+        "metric": "Muon/Dimuon steps/s per matrix batch",
+        "value": round(1000.0 / ms, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "variant": wl.variant, "matrices": wl.count,
+                   "ns_dtype": cfg.ns_dtype, "ns_steps": cfg.ns_steps, "buffer_sets": sets,
+                   "parallelism": "single-gpu"},
+        "matrices_per_s": round(wl.count * 1000.0 / ms, 1),
+        "step_gbs_algorithmic": round(work["hbm_bytes_min"] / (ms * 1e-3) / 1e9, 1),
+        "roofline": roof,
+        "kernel_ms_per_step": {k: round(v[0] / args.steps, 5) for k, v in sorted(per_kind.items())},
+    }
+    if total_flops:
+        out["ns_tflops_algorithmic"] = round(total_flops / (ms * 1e-3) / 1e12, 2)
+    del wl
+    torch.cuda.empty_cache()
+
+    extras = []
+    if args.extra != "none":
+        for item in args.extra.split(","):
+            name, _, var = item.partition(":")
+            wl2 = make_workload(name, dev, var or None)
+            w2 = algorithmic(wl2, is_thin)
+            cfg2, ms2, pk2 = measure(wl2, args.extra_steps, 2, 1)
+            k2, roof2 = roofline_for(wl2, cfg2, pk2, w2, args.extra_steps)
+            tf = 5 * (w2["gram_flops"] + w2["poly_flops"] + w2["comb_flops"])
+            extras.append({"workload": wl2.name, "variant": wl2.variant, "matrices": wl2.count,
+                           "steps": args.extra_steps, "ms_per_step": round(ms2, 4),
+                           "steps_per_s": round(1000.0 / ms2, 3),
+                           "matrices_per_s": round(wl2.count * 1000.0 / ms2, 1),
+                           "ns_tflops_algorithmic": round(tf / (ms2 * 1e-3) / 1e12, 2) if tf else None,
+                           "roofline": roof2,
+                           "kernel_ms_per_step": {k: round(v[0] / args.extra_steps, 4)
+                                                  for k, v in sorted(pk2.items())}})
+            del wl2
+            torch.cuda.empty_cache()
+    out["workloads"] = extras
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(host_sample(args.config, variant), full_count, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,520 @@
+// Host side of the C ABI: argument validation, the batch plan (path choice,
+// workspace layout, tile lists), the descriptor upload cache, and the launch
+// sequence of one Muon / Dimuon step.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "muon_mi355x.h"
+
+namespace muon {
+namespace {
+
+thread_local std::string g_last_error;
+
+// Launch-event hook (timing only).
+struct EventHook {
+  void* const* events = nullptr;
+  int32_t* kinds = nullptr;
+  int32_t n = 0;
+  int32_t next = 0;
+  int32_t last_count = 0;
+};
+thread_local EventHook g_hook;
+
+hipError_t hook_record(int32_t kind, hipStream_t s) {
+  if (!g_hook.events || g_hook.next >= g_hook.n) return hipSuccess;
+  hipError_t e = hipEventRecord(static_cast<hipEvent_t>(g_hook.events[g_hook.next]), s);
+  if (g_hook.kinds) g_hook.kinds[g_hook.next] = kind;
+  ++g_hook.next;
+  return e;
+}
+
+muon_status_t fail(muon_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+constexpr int64_t kMaxDim = 65536;
+constexpr int kThinMaxK = 32;
+constexpr int64_t kThinMaxElems = 32768;   // KP * N held on chip by one workgroup
+constexpr size_t kAlign = 256;
+
+inline int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+inline int64_t ceil_div(int64_t x, int64_t a) { return (x + a - 1) / a; }
+inline int next_pow2(int64_t x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+inline size_t dtype_size(int32_t dt) { return dt == DT_F32 ? 4 : 2; }
+
+bool finite(float x) { return std::isfinite(x); }
+
+// ---------------------------------------------------------------------------
+// Plan
+// ---------------------------------------------------------------------------
+struct Plan {
+  std::vector<MatDesc> desc;
+  std::vector<Tile> k1, k3, syrk, comb, k5;
+  std::vector<uint16_t> gen;
+  // thin matrices grouped by (KP, tall)
+  struct ThinGroup { int kp; bool tall; std::vector<uint16_t> ids; size_t off; };
+  std::vector<ThinGroup> thin;
+  // byte offsets in the workspace
+  size_t desc_off = 0, scal_off = 0, k1_off = 0, k3_off = 0, syrk_off = 0, comb_off = 0, k5_off = 0, gen_off = 0;
+  size_t table_bytes = 0;   // uploaded prefix of the workspace
+  size_t total_bytes = 0;   // whole workspace
+  std::vector<unsigned char> table;
+};
+
+bool is_thin(int64_t m, int64_t n) {
+  const int64_t k = std::min(m, n), N = std::max(m, n);
+  return k <= kThinMaxK && static_cast<int64_t>(next_pow2(k)) * N <= kThinMaxElems;
+}
+
+muon_status_t validate_config(const muon_config_t* cfg) {
+  if (!cfg) return fail(MUON_ERR_INVALID_ARG, "cfg is NULL");
+  const int32_t dts[4] = {cfg->w_dtype, cfg->g_dtype, cfg->mom_dtype, cfg->ns_dtype};
+  for (int32_t dt : dts)
+    if (dt != MUON_F32 && dt != MUON_BF16) return fail(MUON_ERR_DTYPE, "unknown dtype %d", dt);
+  if (cfg->ns_steps < 0 || cfg->ns_steps > kMaxSteps)
+    return fail(MUON_ERR_INVALID_ARG, "ns_steps %d outside [0, %d]", cfg->ns_steps, kMaxSteps);
+  if (!finite(cfg->lr) || !finite(cfg->momentum) || !finite(cfg->weight_decay))
+    return fail(MUON_ERR_INVALID_ARG, "lr, momentum and weight_decay must be finite");
+  if (!finite(cfg->dimuon_eps) || cfg->dimuon_eps < 0.0f)
+    return fail(MUON_ERR_INVALID_ARG, "dimuon_eps must be finite and >= 0");
+  if (cfg->coeff_schedule) {
+    for (int i = 0; i < 3 * cfg->ns_steps; ++i)
+      if (!finite(cfg->coeff_schedule[i])) return fail(MUON_ERR_INVALID_ARG, "coeff_schedule[%d] is not finite", i);
+  } else if (!finite(cfg->a) || !finite(cfg->b) || !finite(cfg->c)) {
+    return fail(MUON_ERR_INVALID_ARG, "coefficients must be finite");
+  }
+  return MUON_OK;
+}
+
+muon_status_t validate_shapes(const muon_matrix_t* mats, int64_t count) {
+  if (!mats) return fail(MUON_ERR_INVALID_ARG, "mats is NULL");
+  if (count < 1) return fail(MUON_ERR_INVALID_ARG, "count %lld < 1", (long long)count);
+  if (count > 65535) return fail(MUON_ERR_UNSUPPORTED, "count %lld > 65535", (long long)count);
+  for (int64_t i = 0; i < count; ++i) {
+    const muon_matrix_t& x = mats[i];
+    if (x.m < 1 || x.n < 1) return fail(MUON_ERR_INVALID_ARG, "matrix %lld: shape %lld x %lld", (long long)i,
+                                        (long long)x.m, (long long)x.n);
+    if (x.m > kMaxDim || x.n > kMaxDim)
+      return fail(MUON_ERR_UNSUPPORTED, "matrix %lld: shape %lld x %lld above %lld", (long long)i, (long long)x.m,
+                  (long long)x.n, (long long)kMaxDim);
+    if (!finite(x.update_scale)) return fail(MUON_ERR_INVALID_ARG, "matrix %lld: update_scale not finite", (long long)i);
+  }
+  return MUON_OK;
+}
+
+struct Range { uintptr_t lo, hi; int64_t mat; const char* what; bool writable; };
+
+muon_status_t validate_buffers(const muon_matrix_t* mats, int64_t count, const muon_config_t* cfg) {
+  std::vector<Range> rs;
+  rs.reserve(count * 5);
+  for (int64_t i = 0; i < count; ++i) {
+    const muon_matrix_t& x = mats[i];
+    const size_t elems = static_cast<size_t>(x.m) * static_cast<size_t>(x.n);
+    struct B { const void* p; size_t bytes; const char* what; bool req; bool wr; } bs[5] = {
+        {x.w, elems * dtype_size(cfg->w_dtype), "w", true, true},
+        {x.g, elems * dtype_size(cfg->g_dtype), "g", true, false},
+        {x.mom, elems * dtype_size(cfg->mom_dtype), "mom", true, true},
+        {x.o_out, elems * 4, "o_out", false, true},
+        {x.energy_out, static_cast<size_t>(x.m + x.n) * 4, "energy_out", false, true}};
+    for (const B& b : bs) {
+      if (!b.p) {
+        if (b.req) return fail(MUON_ERR_INVALID_ARG, "matrix %lld: %s is NULL", (long long)i, b.what);
+        continue;
+      }
+      if (reinterpret_cast<uintptr_t>(b.p) % 16 != 0)
+        return fail(MUON_ERR_INVALID_ARG, "matrix %lld: %s is not 16-byte aligned", (long long)i, b.what);
+      const uintptr_t lo = reinterpret_cast<uintptr_t>(b.p);
+      rs.push_back({lo, lo + b.bytes, i, b.what, b.wr});
+    }
+  }
+  std::sort(rs.begin(), rs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  // Any overlap that involves a written buffer is an error.  Scanning in
+  // address order, keep the written range reaching furthest and the range
+  // (of any kind) reaching furthest.
+  const Range* far_any = nullptr;
+  const Range* far_wr = nullptr;
+  for (const Range& r : rs) {
+    const Range* hit = nullptr;
+    if (r.writable && far_any && far_any->hi > r.lo) hit = far_any;
+    else if (far_wr && far_wr->hi > r.lo) hit = far_wr;
+    if (hit)
+      return fail(MUON_ERR_ALIAS, "matrix %lld %s overlaps matrix %lld %s", (long long)r.mat, r.what,
+                  (long long)hit->mat, hit->what);
+    if (!far_any || r.hi > far_any->hi) far_any = &r;
+    if (r.writable && (!far_wr || r.hi > far_wr->hi)) far_wr = &r;
+  }
+  return MUON_OK;
+}
+
+template <typename T>
+size_t put(std::vector<unsigned char>& buf, size_t off, const std::vector<T>& v) {
+  if (!v.empty()) std::memcpy(buf.data() + off, v.data(), v.size() * sizeof(T));
+  return off;
+}
+
+// Builds the plan.  `with_table` also serialises the uploaded prefix.
+muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_config_t* cfg, bool with_table,
+                         Plan& p) {
+  const size_t es = dtype_size(cfg->ns_dtype);
+  p.desc.assign(count, MatDesc{});
+  std::map<std::pair<int, bool>, std::vector<uint16_t>> thin_groups;
+  for (int64_t i = 0; i < count; ++i) {
+    const muon_matrix_t& x = mats[i];
+    MatDesc& d = p.desc[i];
+    d.g = x.g;
+    d.mom = x.mom;
+    d.w = x.w;
+    d.o_out = x.o_out;
+    d.energy_out = x.energy_out;
+    d.m = static_cast<int32_t>(x.m);
+    d.n = static_cast<int32_t>(x.n);
+    d.k = static_cast<int32_t>(std::min(x.m, x.n));
+    d.N = static_cast<int32_t>(std::max(x.m, x.n));
+    d.tall = x.m > x.n ? 1 : 0;
+    d.update_scale = x.update_scale;
+    d.scal_idx = static_cast<int32_t>(i);
+    d.v_off = -1;
+    if (is_thin(x.m, x.n)) {
+      d.KP = next_pow2(d.k);
+      d.NP = d.N;
+      thin_groups[{d.KP, d.tall != 0}].push_back(static_cast<uint16_t>(i));
+    } else {
+      d.KP = static_cast<int32_t>(round_up(d.k, kPad));
+      d.NP = static_cast<int32_t>(round_up(d.N, kPad));
+      d.ncb = static_cast<int32_t>(ceil_div(d.n, 512));
+      d.nrb = static_cast<int32_t>(ceil_div(d.m, 32));
+      d.n_pn = (d.KP / 64) * (d.NP / 64);
+      d.n_pz = (d.KP / kPad) * (d.NP / kPad);
+      p.gen.push_back(static_cast<uint16_t>(i));
+      for (int rb = 0; rb < d.nrb; ++rb)
+        for (int cb = 0; cb < d.ncb; ++cb) p.k1.push_back({static_cast<uint16_t>(i), (uint16_t)rb, (uint16_t)cb, 0});
+      for (int ti = 0; ti < d.KP / 64; ++ti)
+        for (int tj = 0; tj < d.NP / 64; ++tj) p.k3.push_back({static_cast<uint16_t>(i), (uint16_t)ti, (uint16_t)tj, 0});
+      for (int ti = 0; ti < d.KP / kPad; ++ti)
+        for (int tj = ti; tj < d.KP / kPad; ++tj) p.syrk.push_back({static_cast<uint16_t>(i), (uint16_t)ti, (uint16_t)tj, 0});
+      for (int ti = 0; ti < d.KP / kPad; ++ti)
+        for (int tj = 0; tj < d.NP / kPad; ++tj) p.comb.push_back({static_cast<uint16_t>(i), (uint16_t)ti, (uint16_t)tj, 0});
+      for (int ti = 0; ti < ceil_div(d.m, 64); ++ti)
+        for (int tj = 0; tj < ceil_div(d.n, 64); ++tj) p.k5.push_back({static_cast<uint16_t>(i), (uint16_t)ti, (uint16_t)tj, 0});
+    }
+  }
+  for (auto& kv : thin_groups) p.thin.push_back({kv.first.first, kv.first.second, kv.second, 0});
+
+  // Table prefix: descriptors, scalars, tile lists, id lists.
+  size_t off = kAlign;   // first 256 bytes reserved
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = round_up(off + bytes, kAlign);
+    return o;
+  };
+  p.desc_off = take(sizeof(MatDesc) * count);
+  p.scal_off = take(sizeof(MatScal) * count);
+  p.k1_off = take(sizeof(Tile) * p.k1.size());
+  p.k3_off = take(sizeof(Tile) * p.k3.size());
+  p.syrk_off = take(sizeof(Tile) * p.syrk.size());
+  p.comb_off = take(sizeof(Tile) * p.comb.size());
+  p.k5_off = take(sizeof(Tile) * p.k5.size());
+  p.gen_off = take(sizeof(uint16_t) * p.gen.size());
+  for (auto& g : p.thin) g.off = take(sizeof(uint16_t) * g.ids.size());
+  p.table_bytes = off;
+
+  // Per-matrix scratch of the general path.
+  for (uint16_t i : p.gen) {
+    MatDesc& d = p.desc[i];
+    const size_t kn = static_cast<size_t>(d.KP) * d.NP;
+    for (int b = 0; b < 4; ++b) d.x_off[b] = take(kn * es);
+    d.a_off = take(static_cast<size_t>(d.KP) * d.KP * es);
+    d.b_off = take(static_cast<size_t>(d.KP) * d.KP * es);
+    d.z_off = take(kn * 4);
+    if (cfg->nesterov) d.v_off = take(static_cast<size_t>(d.m) * d.n * 4);
+    d.dr_off = take(static_cast<size_t>(d.m) * 4);
+    d.dc_off = take(static_cast<size_t>(d.n) * 4);
+    d.pr_off = take(static_cast<size_t>(d.ncb) * d.m * 4);
+    d.pc_off = take(static_cast<size_t>(d.nrb) * d.n * 4);
+    d.pn_off = take(static_cast<size_t>(d.n_pn) * 4);
+    d.pz_off = take(static_cast<size_t>(d.n_pz) * 8);
+  }
+  p.total_bytes = off;
+
+  if (with_table) {
+    p.table.assign(p.table_bytes, 0);
+    std::memcpy(p.table.data() + p.desc_off, p.desc.data(), sizeof(MatDesc) * count);
+    put(p.table, p.k1_off, p.k1);
+    put(p.table, p.k3_off, p.k3);
+    put(p.table, p.syrk_off, p.syrk);
+    put(p.table, p.comb_off, p.comb);
+    put(p.table, p.k5_off, p.k5);
+    put(p.table, p.gen_off, p.gen);
+    for (auto& g : p.thin) put(p.table, g.off, g.ids);
+  }
+  return MUON_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Descriptor upload cache, keyed by workspace address
+// ---------------------------------------------------------------------------
+struct CacheEntry {
+  std::vector<unsigned char> table;   // what the workspace prefix holds
+  void* pinned = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool ev_pending = false;
+};
+
+std::mutex g_cache_mu;
+std::map<uintptr_t, CacheEntry> g_cache;
+
+muon_status_t upload_table(const Plan& p, void* ws, hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  CacheEntry& e = g_cache[reinterpret_cast<uintptr_t>(ws)];
+  if (e.table == p.table) return MUON_OK;
+  hipError_t err;
+  if (e.ev_pending) {
+    if ((err = hipEventSynchronize(e.ev)) != hipSuccess)
+      return fail(MUON_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(err));
+    e.ev_pending = false;
+  }
+  if (e.cap < p.table.size()) {
+    if (e.pinned) (void)hipHostFree(e.pinned);
+    e.pinned = nullptr;
+    e.cap = 0;
+    if ((err = hipHostMalloc(&e.pinned, p.table.size(), hipHostMallocDefault)) != hipSuccess) {
+      e.pinned = nullptr;
+      e.table.clear();
+      return fail(MUON_ERR_HIP, "hipHostMalloc(%zu): %s", p.table.size(), hipGetErrorString(err));
+    }
+    e.cap = p.table.size();
+  }
+  if (!e.ev) {
+    if ((err = hipEventCreateWithFlags(&e.ev, hipEventDisableTiming)) != hipSuccess) {
+      e.ev = nullptr;
+      e.table.clear();
+      return fail(MUON_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(err));
+    }
+  }
+  std::memcpy(e.pinned, p.table.data(), p.table.size());
+  if ((err = hipMemcpyAsync(ws, e.pinned, p.table.size(), hipMemcpyHostToDevice, stream)) != hipSuccess) {
+    e.table.clear();
+    return fail(MUON_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(err));
+  }
+  if ((err = hipEventRecord(e.ev, stream)) != hipSuccess) {
+    e.table.clear();
+    return fail(MUON_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(err));
+  }
+  e.ev_pending = true;
+  e.table = p.table;
+  return MUON_OK;
+}
+
+// ---------------------------------------------------------------------------
+// One step
+// ---------------------------------------------------------------------------
+#define MUON_HIP_TRY(expr)                                                                 \
+  do {                                                                                     \
+    hipError_t e_ = (expr);                                                                \
+    if (e_ != hipSuccess) return fail(MUON_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+// Launch, then record the hook's event for this launch kind.
+#define MUON_LAUNCH(kind, expr)              \
+  do {                                       \
+    MUON_HIP_TRY(expr);                      \
+    MUON_HIP_TRY(hook_record((kind), s));    \
+  } while (0)
+
+muon_status_t run_step(const muon_matrix_t* mats, int64_t count, const muon_config_t* cfg, void* ws,
+                       size_t ws_bytes, void* stream_ptr, bool dimuon) {
+  g_last_error.clear();
+  muon_status_t st;
+  if ((st = validate_config(cfg)) != MUON_OK) return st;
+  if ((st = validate_shapes(mats, count)) != MUON_OK) return st;
+  if ((st = validate_buffers(mats, count, cfg)) != MUON_OK) return st;
+  Plan p;
+  if ((st = build_plan(mats, count, cfg, true, p)) != MUON_OK) return st;
+  if (!ws) return fail(MUON_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return fail(MUON_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (ws_bytes < p.total_bytes)
+    return fail(MUON_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, p.total_bytes);
+  // The workspace must not overlap any caller buffer.
+  {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(ws), hi = lo + p.total_bytes;
+    for (int64_t i = 0; i < count; ++i) {
+      const muon_matrix_t& x = mats[i];
+      const size_t elems = static_cast<size_t>(x.m) * x.n;
+      const void* ps[5] = {x.w, x.g, x.mom, x.o_out, x.energy_out};
+      const size_t bytes[5] = {elems * dtype_size(cfg->w_dtype), elems * dtype_size(cfg->g_dtype),
+                               elems * dtype_size(cfg->mom_dtype), elems * 4,
+                               static_cast<size_t>(x.m + x.n) * 4};
+      for (int b = 0; b < 5; ++b) {
+        if (!ps[b]) continue;
+        const uintptr_t plo = reinterpret_cast<uintptr_t>(ps[b]);
+        if (plo < hi && lo < plo + bytes[b])
+          return fail(MUON_ERR_ALIAS, "matrix %lld buffer %d overlaps the workspace", (long long)i, b);
+      }
+    }
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream_ptr);
+  if ((st = upload_table(p, ws, s)) != MUON_OK) return st;
+
+  char* base = static_cast<char*>(ws);
+  StepArgs a{};
+  a.desc = reinterpret_cast<const MatDesc*>(base + p.desc_off);
+  a.scal = reinterpret_cast<MatScal*>(base + p.scal_off);
+  a.ws = base;
+  a.mu = cfg->momentum;
+  a.lr = cfg->lr;
+  a.eps = cfg->dimuon_eps;
+  a.weight_decay = cfg->weight_decay;
+  a.g_dt = cfg->g_dtype;
+  a.mom_dt = cfg->mom_dtype;
+  a.w_dt = cfg->w_dtype;
+  a.ns_dt = cfg->ns_dtype;
+  a.nesterov = cfg->nesterov ? 1 : 0;
+  a.dimuon = dimuon ? 1 : 0;
+
+  Coeffs cf[kMaxSteps];
+  for (int t = 0; t < cfg->ns_steps; ++t) {
+    if (cfg->coeff_schedule)
+      cf[t] = {cfg->coeff_schedule[3 * t], cfg->coeff_schedule[3 * t + 1], cfg->coeff_schedule[3 * t + 2]};
+    else
+      cf[t] = {cfg->a, cfg->b, cfg->c};
+  }
+
+  auto tl = [&](size_t off) { return reinterpret_cast<const Tile*>(base + off); };
+  auto il = [&](size_t off) { return reinterpret_cast<const uint16_t*>(base + off); };
+
+  g_hook.next = 0;
+  MUON_HIP_TRY(hook_record(MUON_LAUNCH_START, s));
+  for (const auto& g : p.thin)
+    MUON_LAUNCH(MUON_LAUNCH_THIN,
+                launch_thin(a, il(g.off), static_cast<int>(g.ids.size()), g.kp, g.tall, cfg->ns_steps, cf, s));
+
+  if (!p.gen.empty()) {
+    const int ng = static_cast<int>(p.gen.size());
+    MUON_LAUNCH(MUON_LAUNCH_MOMENTUM, launch_momentum(a, tl(p.k1_off), static_cast<int>(p.k1.size()), dimuon, s));
+    if (dimuon) MUON_LAUNCH(MUON_LAUNCH_CONDITION, launch_condition(a, il(p.gen_off), ng, s));
+    MUON_LAUNCH(MUON_LAUNCH_PRESCALE, launch_prescale(a, tl(p.k3_off), static_cast<int>(p.k3.size()), s));
+    MUON_LAUNCH(MUON_LAUNCH_NORM, launch_norm_finalize(a, il(p.gen_off), ng, s));
+    const int nsyrk = static_cast<int>(p.syrk.size()), ncomb = static_cast<int>(p.comb.size());
+    if (cfg->ns_steps == 0) {
+      MUON_LAUNCH(MUON_LAUNCH_COMBINE,
+                  launch_combine(a, tl(p.comb_off), ncomb, 0, 1, true, true, false, Coeffs{1.0f, 0.0f, 0.0f}, s));
+    }
+    for (int t = 0; t < cfg->ns_steps; ++t) {
+      const int src = t & 1, dst = src ^ 1;
+      const bool first = t == 0, last = t == cfg->ns_steps - 1;
+      MUON_LAUNCH(MUON_LAUNCH_GRAM, launch_syrk(a, tl(p.syrk_off), nsyrk, 0, src, first, cf[t], s));
+      MUON_LAUNCH(MUON_LAUNCH_POLY, launch_syrk(a, tl(p.syrk_off), nsyrk, 1, src, first, cf[t], s));
+      MUON_LAUNCH(MUON_LAUNCH_COMBINE, launch_combine(a, tl(p.comb_off), ncomb, src, dst, first, last, true, cf[t], s));
+    }
+    if (dimuon) MUON_LAUNCH(MUON_LAUNCH_POSTNORM, launch_post_finalize(a, il(p.gen_off), ng, s));
+    MUON_LAUNCH(MUON_LAUNCH_UPDATE, launch_update(a, tl(p.k5_off), static_cast<int>(p.k5.size()), s));
+  }
+  g_hook.last_count = g_hook.next;
+  return MUON_OK;
+}
+
+}  // namespace
+}  // namespace muon
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+void muon_config_default(muon_config_t* cfg) {
+  if (!cfg) return;
+  std::memset(cfg, 0, sizeof(*cfg));
+  cfg->lr = 0.02f;
+  cfg->momentum = 0.95f;
+  cfg->ns_steps = 5;
+  cfg->a = 3.4445f;
+  cfg->b = -4.7750f;
+  cfg->c = 2.0315f;
+  cfg->coeff_schedule = nullptr;
+  cfg->w_dtype = MUON_BF16;
+  cfg->g_dtype = MUON_BF16;
+  cfg->mom_dtype = MUON_BF16;
+  cfg->ns_dtype = MUON_BF16;
+  cfg->dimuon_eps = 1e-4f;
+  cfg->nesterov = 0;
+  cfg->weight_decay = 0.0f;
+}
+
+muon_status_t muon_workspace_bytes(const muon_matrix_t* mats, int64_t count, const muon_config_t* cfg,
+                                   size_t* bytes) {
+  using namespace muon;
+  g_last_error.clear();
+  if (!bytes) return fail(MUON_ERR_INVALID_ARG, "bytes is NULL");
+  muon_status_t st;
+  if ((st = validate_config(cfg)) != MUON_OK) return st;
+  if ((st = validate_shapes(mats, count)) != MUON_OK) return st;
+  Plan p;
+  if ((st = build_plan(mats, count, cfg, false, p)) != MUON_OK) return st;
+  *bytes = p.total_bytes;
+  return MUON_OK;
+}
+
+muon_status_t muon_step(const muon_matrix_t* mats, int64_t count, const muon_config_t* cfg, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return muon::run_step(mats, count, cfg, workspace, workspace_bytes, stream, false);
+}
+
+muon_status_t dimuon_step(const muon_matrix_t* mats, int64_t count, const muon_config_t* cfg, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return muon::run_step(mats, count, cfg, workspace, workspace_bytes, stream, true);
+}
+
+int32_t muon_set_launch_events(void* const* events, int32_t* kinds, int32_t n) {
+  const int32_t last = muon::g_hook.last_count;
+  muon::g_hook.events = events;
+  muon::g_hook.kinds = kinds;
+  muon::g_hook.n = events ? (n > 0 ? n : 0) : 0;
+  muon::g_hook.next = 0;
+  return last;
+}
+
+void muon_workspace_invalidate(void* workspace) {
+  std::lock_guard<std::mutex> lock(muon::g_cache_mu);
+  auto it = muon::g_cache.find(reinterpret_cast<uintptr_t>(workspace));
+  if (it != muon::g_cache.end()) it->second.table.clear();
+}
+
+const char* muon_status_string(muon_status_t status) {
+  switch (status) {
+    case MUON_OK: return "ok";
+    case MUON_ERR_INVALID_ARG: return "invalid argument";
+    case MUON_ERR_DTYPE: return "unsupported dtype";
+    case MUON_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MUON_ERR_ALIAS: return "buffers overlap";
+    case MUON_ERR_HIP: return "HIP runtime error";
+    case MUON_ERR_UNSUPPORTED: return "unsupported shape or count";
+  }
+  return "unknown status";
+}
+
+const char* muon_last_error(void) { return muon::g_last_error.c_str(); }
+
+int32_t muon_abi_version(void) { return MUON_ABI_VERSION; }
+
+}  // extern "C"

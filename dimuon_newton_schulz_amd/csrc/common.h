@@ -1,0 +1,217 @@
+// Internal definitions shared by the gfx950 kernels and the host planner.
+//
+// Layout of one general-path matrix in the workspace (Gram orientation):
+// the matrix is viewed as k x N with k = min(m, n) and N = max(m, n);
+// a tall matrix (m > n) is stored transposed.  Every workspace matrix is
+// padded with zeros to multiples of kPad in both dimensions, and every
+// kernel writes whole padded tiles, so the padding stays zero through all
+// iterations and the GEMM kernels need no bounds checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+constexpr int kPad = 128;          // padding granularity of workspace matrices
+constexpr int kMaxSteps = 32;      // largest ns_steps accepted
+
+enum DType : int32_t { DT_F32 = 0, DT_BF16 = 1 };
+
+// Per-matrix device descriptor (uploaded once per batch into the workspace).
+struct alignas(16) MatDesc {
+  const void* g;          // caller: gradient (g dtype), m x n
+  void* mom;              // caller: momentum (mom dtype), m x n
+  void* w;                // caller: weights (w dtype), m x n
+  float* o_out;           // caller, optional: O (f32), m x n
+  float* energy_out;      // caller, optional: R (m) then C (n)
+  int32_t m, n;           // original shape
+  int32_t k, N;           // Gram side and long side
+  int32_t KP, NP;         // padded k, N (general path)
+  int32_t tall;           // m > n: the Gram orientation is the transpose
+  float update_scale;
+  int64_t x_off[4];       // X (KP x NP) and X^T (NP x KP), ping (0,1) and pong (2,3), ns dtype
+  int64_t a_off;          // A = X X^T, KP x KP, ns dtype
+  int64_t b_off;          // B = bA + c A A, KP x KP, ns dtype
+  int64_t z_off;          // Z (last iterate), KP x NP, f32
+  int64_t v_off;          // Nesterov input, m x n f32 (or -1)
+  int64_t dr_off;         // row factors, m f32
+  int64_t dc_off;         // column factors, n f32
+  int64_t pr_off;         // row-energy partials [ncb][m] f32
+  int64_t pc_off;         // column-energy partials [nrb][n] f32
+  int64_t pn_off;         // ||Y||^2 partials, one per prescale tile, f32
+  int64_t pz_off;         // (||Z||^2, ||P||^2) partials, one pair per combine tile, f32
+  int32_t ncb, nrb;       // number of 512-column / 32-row energy blocks
+  int32_t n_pn, n_pz;     // partial counts
+  int32_t scal_idx;       // index into the per-matrix scalar array
+  int32_t pad0;
+};
+
+// Per-matrix scalars written on the device during a step.
+struct alignas(16) MatScal {
+  float inv_nu;           // 1 / ||Y||_F (0 if the norm is 0)
+  float inv_nu2;          // inv_nu^2
+  float post;             // Dimuon norm fix ||Z|| / ||P|| (1 for Muon)
+  float cond_on;          // 1 if the Dimuon factors are active
+};
+
+// One work tile: matrix index in the descriptor table and tile coordinates.
+struct alignas(8) Tile {
+  uint16_t mat, ti, tj, aux;
+};
+
+// Coefficients of every iteration, passed by value to the GEMM kernels.
+struct Coeffs {
+  float a, b, c;
+};
+
+// Everything a step's kernels need besides the tile lists.
+struct StepArgs {
+  const MatDesc* desc;    // device
+  MatScal* scal;          // device
+  char* ws;               // workspace base (device)
+  float mu, lr, eps, weight_decay;
+  int32_t g_dt, mom_dt, w_dt, ns_dt;
+  int32_t nesterov;
+  int32_t dimuon;
+};
+
+// --------------------------------------------------------------------------
+// Device helpers
+// --------------------------------------------------------------------------
+#if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round-to-nearest-even float -> bfloat16 bits; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float load_elem(const void* p, int64_t idx, int32_t dt) {
+  if (dt == DT_F32) return static_cast<const float*>(p)[idx];
+  return bf16_to_f32(static_cast<const uint16_t*>(p)[idx]);
+}
+
+__device__ __forceinline__ void store_elem(void* p, int64_t idx, int32_t dt, float v) {
+  if (dt == DT_F32) static_cast<float*>(p)[idx] = v;
+  else static_cast<uint16_t*>(p)[idx] = f32_to_bf16(v);
+}
+
+// Value a tensor of dtype dt holds after storing v.
+__device__ __forceinline__ float round_to(float v, int32_t dt) {
+  if (dt == DT_F32) return v;
+  return bf16_to_f32(f32_to_bf16(v));
+}
+
+// Four consecutive elements starting at idx (idx % 4 == 0 and the base
+// aligned for the dtype's 4-element vector: 16 bytes f32, 8 bytes bf16).
+__device__ __forceinline__ void load4_aligned(const void* p, int64_t idx, int32_t dt, float out[4]) {
+  if (dt == DT_F32) {
+    float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + idx);
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+  } else {
+    uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + idx);
+    out[0] = __uint_as_float(v.x << 16);
+    out[1] = __uint_as_float(v.x & 0xffff0000u);
+    out[2] = __uint_as_float(v.y << 16);
+    out[3] = __uint_as_float(v.y & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ void store4_aligned(void* p, int64_t idx, int32_t dt, const float v[4]) {
+  if (dt == DT_F32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(p) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    uint2 u;
+    u.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+    u.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + idx) = u;
+  }
+}
+
+// Wave64 butterfly sum: after it every lane holds the pairwise-tree sum of
+// the 64 lane values (lane groups of 2, 4, ... 64 combined left + right;
+// IEEE addition is commutative, so lane L and lane L^off agree).
+__device__ __forceinline__ float wave_tree_sum(float v) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) v = v + __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) v = v + __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Pairwise-tree sum of p[0], p[stride], ..., p[(count-1)*stride], zero-padded
+// to a power of two: a binary counter keeps one partial per complete block.
+__device__ __forceinline__ float pairwise_strided(const float* p, int count, int64_t stride) {
+  float stack[24];
+  int pow2 = 1;
+  while (pow2 < count) pow2 <<= 1;
+  for (int t = 0; t < pow2; ++t) {
+    float carry = (t < count) ? p[static_cast<int64_t>(t) * stride] : 0.0f;
+    int j = 0;
+    while ((t >> j) & 1) {
+      carry = stack[j] + carry;   // earlier (left) block + later (right) block
+      ++j;
+    }
+    stack[j] = carry;
+  }
+  int top = 0;
+  while ((1 << top) < pow2) ++top;
+  return stack[top];
+}
+
+// Conditioning factor (relative energy + eps)^(-1/4).
+__device__ __forceinline__ float cond_factor(float e, float emax, float eps) {
+  float rho = e / emax;
+  float t = rho + eps;
+  return 1.0f / sqrtf(sqrtf(t));
+}
+
+#endif  // device
+
+// --------------------------------------------------------------------------
+// Host-side launchers (defined in the .hip files)
+// --------------------------------------------------------------------------
+struct LaunchLists {
+  const Tile* k1;      int n_k1;     // momentum + energy partials tiles (general path)
+  const Tile* k3;      int n_k3;     // prescale tiles
+  const Tile* syrk;    int n_syrk;   // upper-triangular Gram tiles
+  const Tile* comb;    int n_comb;   // combine tiles
+  const Tile* k5;      int n_k5;     // final update tiles
+  const uint16_t* gen; int n_gen;    // general-path matrix ids
+  const uint16_t* thin; int n_thin;  // thin-path matrix ids (grouped by padded k)
+};
+
+hipError_t launch_momentum(const StepArgs& a, const Tile* tiles, int n, bool energies, hipStream_t s);
+hipError_t launch_condition(const StepArgs& a, const uint16_t* mats, int n, hipStream_t s);
+hipError_t launch_prescale(const StepArgs& a, const Tile* tiles, int n, hipStream_t s);
+hipError_t launch_norm_finalize(const StepArgs& a, const uint16_t* mats, int n, hipStream_t s);
+hipError_t launch_post_finalize(const StepArgs& a, const uint16_t* mats, int n, hipStream_t s);
+hipError_t launch_update(const StepArgs& a, const Tile* tiles, int n, hipStream_t s);
+// Gram / polynomial (kind 0: A = alpha X X^T, kind 1: B = c A A + b A) and combine.
+hipError_t launch_syrk(const StepArgs& a, const Tile* tiles, int n, int kind, int src_x,
+                       bool first, Coeffs cf, hipStream_t s);
+// Combine X' = alpha (a X + B X); src/dst select the ping (0) or pong (1)
+// buffers; `product` false skips B X (used when ns_steps is 0).
+hipError_t launch_combine(const StepArgs& a, const Tile* tiles, int n, int src_x, int dst_x,
+                          bool first, bool last, bool product, Coeffs cf, hipStream_t s);
+hipError_t launch_thin(const StepArgs& a, const uint16_t* mats, int n, int kp, bool tall,
+                       int ns_steps, const Coeffs* cf, hipStream_t s);
+
+}  // namespace muon

@@ -1,0 +1,463 @@
+// HBM-streaming kernels of the general path: momentum (+ Dimuon energies),
+// conditioning, prescale into the Gram orientation, norm finalisation, and
+// the final update.  No FMA contraction in this file: the energies must
+// follow the stated float32 tree exactly, so every fused multiply-add below
+// is written out as __builtin_fmaf.
+#pragma clang fp contract(off)
+
+#include "common.h"
+
+namespace muon {
+
+// ---------------------------------------------------------------------------
+// Loads of 8 consecutive row elements (columns col0 .. col0+7); columns at or
+// beyond n read as 0.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void load8(const void* p, int32_t dt, int64_t rowoff, int col0, int n,
+                                      float out[8]) {
+  const bool full = col0 + 8 <= n;
+  const bool al = (dt == DT_F32) ? ((n & 3) == 0) : ((n & 7) == 0);
+  if (full && al) {
+    if (dt == DT_F32) {
+      const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p) + rowoff + col0);
+      float4 a = q[0], b = q[1];
+      out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+      out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+    } else {
+      uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + rowoff + col0);
+      out[0] = __uint_as_float(v.x << 16); out[1] = __uint_as_float(v.x & 0xffff0000u);
+      out[2] = __uint_as_float(v.y << 16); out[3] = __uint_as_float(v.y & 0xffff0000u);
+      out[4] = __uint_as_float(v.z << 16); out[5] = __uint_as_float(v.z & 0xffff0000u);
+      out[6] = __uint_as_float(v.w << 16); out[7] = __uint_as_float(v.w & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      out[e] = (col0 + e < n) ? load_elem(p, rowoff + col0 + e, dt) : 0.0f;
+  }
+}
+
+__device__ __forceinline__ void store8(void* p, int32_t dt, int64_t rowoff, int col0, int n,
+                                       const float v[8]) {
+  const bool full = col0 + 8 <= n;
+  const bool al = (dt == DT_F32) ? ((n & 3) == 0) : ((n & 7) == 0);
+  if (full && al) {
+    if (dt == DT_F32) {
+      float4* q = reinterpret_cast<float4*>(static_cast<float*>(p) + rowoff + col0);
+      q[0] = make_float4(v[0], v[1], v[2], v[3]);
+      q[1] = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+      uint4 u;
+      u.x = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+      u.y = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+      u.z = f32_to_bf16(v[4]) | (static_cast<uint32_t>(f32_to_bf16(v[5])) << 16);
+      u.w = f32_to_bf16(v[6]) | (static_cast<uint32_t>(f32_to_bf16(v[7])) << 16);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p) + rowoff + col0) = u;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (col0 + e < n) store_elem(p, rowoff + col0 + e, dt, v[e]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K1: M_t = mu * M_{t-1} + G, written in the momentum dtype; optionally the
+// Nesterov input G + mu * M_t (f32, workspace); optionally the float32
+// energy partials of M_{t-1}.
+//
+// Tile: 32 rows x 512 columns; wave w owns rows 8w .. 8w+7, lane l owns
+// columns 8l .. 8l+7.  Row partial over the tile's 512 columns: in-lane
+// pairwise over 8, then the wave butterfly -> pr[cb][row].  Column partial
+// over the tile's 32 rows: in-lane pairwise over the wave's 8 rows, then the
+// four waves pairwise -> pc[rb][col].  Both are aligned power-of-two blocks
+// of the stated tree.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_momentum(StepArgs a, const Tile* __restrict__ tiles,
+                                                  int energies) {
+  __shared__ float red[4][512];
+  const Tile t = tiles[blockIdx.x];
+  const MatDesc& d = a.desc[t.mat];
+  const int m = d.m, n = d.n;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col0 = t.tj * 512 + lane * 8;
+  const int row_base = t.ti * 32 + wave * 8;
+  float* vbuf = (a.nesterov && d.v_off >= 0) ? reinterpret_cast<float*>(a.ws + d.v_off) : nullptr;
+
+  // Binary-counter pairwise over the wave's 8 rows, per column.
+  float lvl0[8], lvl1[8], lvl2[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int row = row_base + r;
+    float mp[8], g[8], mn[8];
+    const bool in = row < m;
+    const int64_t off = static_cast<int64_t>(row) * n;
+    if (in) {
+      load8(d.mom, a.mom_dt, off, col0, n, mp);
+      load8(d.g, a.g_dt, off, col0, n, g);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { mp[e] = 0.0f; g[e] = 0.0f; }
+    }
+    if (energies) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = mp[e] * mp[e];
+      // row partial: in-lane pairwise over 8, then the butterfly over 64 lanes
+      float s = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      s = wave_tree_sum(s);
+      if (in && lane == 0)
+        reinterpret_cast<float*>(a.ws + d.pr_off)[static_cast<int64_t>(t.tj) * m + row] = s;
+      // column partial: binary counter over r
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if ((r & 1) == 0) {
+          lvl0[e] = p[e];
+        } else {
+          float c1 = lvl0[e] + p[e];
+          if ((r & 2) == 0) {
+            lvl1[e] = c1;
+          } else {
+            float c2 = lvl1[e] + c1;
+            if ((r & 4) == 0) lvl2[e] = c2;
+            else lvl2[e] = lvl2[e] + c2;
+          }
+        }
+      }
+    }
+    if (in) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mn[e] = round_to(__builtin_fmaf(a.mu, mp[e], g[e]), a.mom_dt);
+      store8(d.mom, a.mom_dt, off, col0, n, mn);
+      if (vbuf) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = g[e] + a.mu * mn[e];
+        store8(vbuf, DT_F32, off, col0, n, v);
+      }
+    }
+  }
+  if (!energies) return;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[wave][lane * 8 + e] = lvl2[e];
+  __syncthreads();
+  float* pc = reinterpret_cast<float*>(a.ws + d.pc_off);
+  for (int c = threadIdx.x; c < 512; c += 256) {
+    const int col = t.tj * 512 + c;
+    if (col < n) {
+      float s = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
+      pc[static_cast<int64_t>(t.ti) * n + col] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K2: energies from the partials (pairwise over blocks), then the factors.
+// One workgroup per matrix.  R, C are staged in the factor arrays, converted
+// in place once the maxima are known.
+// ---------------------------------------------------------------------------
+__device__ float block_max(float v, float* sh) {
+  v = wave_max(v);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  float r = sh[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = fmaxf(r, sh[w]);
+  return r;
+}
+
+__global__ __launch_bounds__(256) void k_condition(StepArgs a, const uint16_t* __restrict__ mats) {
+  __shared__ float sh[8];
+  const int mat = mats[blockIdx.x];
+  const MatDesc& d = a.desc[mat];
+  const int m = d.m, n = d.n;
+  float* dr = reinterpret_cast<float*>(a.ws + d.dr_off);
+  float* dc = reinterpret_cast<float*>(a.ws + d.dc_off);
+  const float* pr = reinterpret_cast<const float*>(a.ws + d.pr_off);
+  const float* pc = reinterpret_cast<const float*>(a.ws + d.pc_off);
+  float rmax = 0.0f, cmax = 0.0f;
+  for (int i = threadIdx.x; i < m; i += blockDim.x) {
+    float e = pairwise_strided(pr + i, d.ncb, m);
+    dr[i] = e;
+    if (d.energy_out) d.energy_out[i] = e;
+    rmax = fmaxf(rmax, e);
+  }
+  for (int j = threadIdx.x; j < n; j += blockDim.x) {
+    float e = pairwise_strided(pc + j, d.nrb, n);
+    dc[j] = e;
+    if (d.energy_out) d.energy_out[m + j] = e;
+    cmax = fmaxf(cmax, e);
+  }
+  rmax = block_max(rmax, sh);
+  cmax = block_max(cmax, sh);
+  // A zero previous momentum (all energies 0) switches the conditioning off.
+  const bool on = rmax > 0.0f && cmax > 0.0f;
+  for (int i = threadIdx.x; i < m; i += blockDim.x) dr[i] = on ? cond_factor(dr[i], rmax, a.eps) : 1.0f;
+  for (int j = threadIdx.x; j < n; j += blockDim.x) dc[j] = on ? cond_factor(dc[j], cmax, a.eps) : 1.0f;
+  if (threadIdx.x == 0) a.scal[d.scal_idx].cond_on = on ? 1.0f : 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// K3: Y = D_R * V * D_C (V = M_t, or the Nesterov input), rounded to the NS
+// dtype, written in the Gram orientation (KP x NP) and its transpose
+// (NP x KP), zero in the padding; one ||Y||^2 partial per tile.
+// Tile: 64 x 64 of the Gram orientation; the source tile goes through LDS.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_prescale(StepArgs a, const Tile* __restrict__ tiles) {
+  __shared__ float tileS[64][65];
+  __shared__ float red[4];
+  const Tile t = tiles[blockIdx.x];
+  const MatDesc& d = a.desc[t.mat];
+  const int m = d.m, n = d.n;
+  const int tid = threadIdx.x;
+  const bool cond = a.dimuon && a.scal[d.scal_idx].cond_on != 0.0f;
+  const float* dr = reinterpret_cast<const float*>(a.ws + d.dr_off);
+  const float* dc = reinterpret_cast<const float*>(a.ws + d.dc_off);
+  const bool use_v = a.nesterov && d.v_off >= 0;
+  const void* src = use_v ? static_cast<const void*>(a.ws + d.v_off) : static_cast<const void*>(d.mom);
+  const int sdt = use_v ? DT_F32 : a.mom_dt;
+
+  // Source tile in the original orientation: rows si0.., cols sj0..
+  // Gram element (ga, gb) <- source (ga, gb) when wide, (gb, ga) when tall.
+  const int ga0 = t.ti * 64, gb0 = t.tj * 64;
+  const int si0 = d.tall ? gb0 : ga0;
+  const int sj0 = d.tall ? ga0 : gb0;
+  {
+    const int r = tid >> 2, c0 = (tid & 3) * 16;
+    const int row = si0 + r;
+    float v[16];
+    if (row < m) {
+      const int64_t off = static_cast<int64_t>(row) * n;
+      load8(src, sdt, off, sj0 + c0, n, v);
+      load8(src, sdt, off, sj0 + c0 + 8, n, v + 8);
+      const float rf = cond ? dr[row] : 1.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int col = sj0 + c0 + e;
+        const float cf = (cond && col < n) ? dc[col] : 1.0f;
+        v[e] = (rf * v[e]) * cf;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) tileS[r][c0 + e] = round_to(v[e], a.ns_dt);
+  }
+  __syncthreads();
+  // Write Y (Gram orientation) and Y^T, 16 contiguous elements per thread.
+  char* ybase = a.ws + d.x_off[0];
+  char* ytbase = a.ws + d.x_off[1];
+  const int r = tid >> 2, c0 = (tid & 3) * 16;
+  float ssq = 0.0f;
+  {
+    // Y[ga0 + r][gb0 + c0 + e] = (wide) S[r][c0+e] | (tall) S[c0+e][r]
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = d.tall ? tileS[c0 + e][r] : tileS[r][c0 + e];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ssq = ssq + v[e] * v[e];
+    const int64_t off = static_cast<int64_t>(ga0 + r) * d.NP + gb0 + c0;
+    if (a.ns_dt == DT_F32) {
+      float4* q = reinterpret_cast<float4*>(reinterpret_cast<float*>(ybase) + off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q[e] = make_float4(v[4 * e], v[4 * e + 1], v[4 * e + 2], v[4 * e + 3]);
+    } else {
+      uint4* q = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(ybase) + off);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        uint4 u;
+        u.x = f32_to_bf16(v[8 * e + 0]) | (static_cast<uint32_t>(f32_to_bf16(v[8 * e + 1])) << 16);
+        u.y = f32_to_bf16(v[8 * e + 2]) | (static_cast<uint32_t>(f32_to_bf16(v[8 * e + 3])) << 16);
+        u.z = f32_to_bf16(v[8 * e + 4]) | (static_cast<uint32_t>(f32_to_bf16(v[8 * e + 5])) << 16);
+        u.w = f32_to_bf16(v[8 * e + 6]) | (static_cast<uint32_t>(f32_to_bf16(v[8 * e + 7])) << 16);
+        q[e] = u;
+      }
+    }
+  }
+  {
+    // Y^T[gb0 + r][ga0 + c0 + e] = Y[ga0 + c0 + e][gb0 + r]
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = d.tall ? tileS[r][c0 + e] : tileS[c0 + e][r];
+    const int64_t off = static_cast<int64_t>(gb0 + r) * d.KP + ga0 + c0;
+    if (a.ns_dt == DT_F32) {
+      float4* q = reinterpret_cast<float4*>(reinterpret_cast<float*>(ytbase) + off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q[e] = make_float4(v[4 * e], v[4 * e + 1], v[4 * e + 2], v[4 * e + 3]);
+    } else {
+      uint4* q = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(ytbase) + off);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        uint4 u;
+        u.x = f32_to_bf16(v[8 * e + 0]) | (static_cast<uint32_t>(f32_to_bf16(v[8 * e + 1])) << 16);
+        u.y = f32_to_bf16(v[8 * e + 2]) | (static_cast<uint32_t>(f32_to_bf16(v[8 * e + 3])) << 16);
+        u.z = f32_to_bf16(v[8 * e + 4]) | (static_cast<uint32_t>(f32_to_bf16(v[8 * e + 5])) << 16);
+        u.w = f32_to_bf16(v[8 * e + 6]) | (static_cast<uint32_t>(f32_to_bf16(v[8 * e + 7])) << 16);
+        q[e] = u;
+      }
+    }
+  }
+  ssq = wave_tree_sum(ssq);
+  if ((tid & 63) == 0) red[tid >> 6] = ssq;
+  __syncthreads();
+  if (tid == 0) {
+    const float s = (red[0] + red[1]) + (red[2] + red[3]);
+    const int tiles_per_row = d.NP / 64;
+    reinterpret_cast<float*>(a.ws + d.pn_off)[t.ti * tiles_per_row + t.tj] = s;
+  }
+}
+
+// Deterministic block sum: fixed per-thread stride order, butterfly, waves in order.
+__device__ float block_sum_fixed(const float* p, int count, float* sh) {
+  float s = 0.0f;
+  for (int i = threadIdx.x; i < count; i += blockDim.x) s = s + p[i];
+  s = wave_tree_sum(s);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) sh[wave] = s;
+  __syncthreads();
+  float r = sh[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = r + sh[w];
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// ||Y||_F from the prescale partials.  One workgroup per matrix.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_norm_finalize(StepArgs a, const uint16_t* __restrict__ mats) {
+  __shared__ float sh[8];
+  const int mat = mats[blockIdx.x];
+  const MatDesc& d = a.desc[mat];
+  const float nu2 = block_sum_fixed(reinterpret_cast<const float*>(a.ws + d.pn_off), d.n_pn, sh);
+  if (threadIdx.x == 0) {
+    MatScal& s = a.scal[d.scal_idx];
+    const float inv = (nu2 == 0.0f) ? 0.0f : 1.0f / sqrtf(nu2);
+    s.inv_nu = inv;
+    s.inv_nu2 = inv * inv;
+    s.post = 1.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dimuon norm fix ||Z||_F / ||D_R Z D_C||_F from the last combine's partials.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_post_finalize(StepArgs a, const uint16_t* __restrict__ mats) {
+  __shared__ float sh[8];
+  __shared__ float zsum;
+  const int mat = mats[blockIdx.x];
+  const MatDesc& d = a.desc[mat];
+  const float* pz = reinterpret_cast<const float*>(a.ws + d.pz_off);
+  // partials are interleaved pairs (||Z||^2, ||P||^2)
+  float sz = 0.0f, sp = 0.0f;
+  for (int i = threadIdx.x; i < d.n_pz; i += blockDim.x) {
+    sz = sz + pz[2 * i];
+    sp = sp + pz[2 * i + 1];
+  }
+  sz = wave_tree_sum(sz);
+  sp = wave_tree_sum(sp);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) sh[wave] = sz;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = sh[0];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = r + sh[w];
+    zsum = r;
+  }
+  __syncthreads();
+  if (lane == 0) sh[wave] = sp;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = sh[0];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = r + sh[w];
+    a.scal[d.scal_idx].post = (r == 0.0f) ? 0.0f : sqrtf(zsum) / sqrtf(r);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K5: O = post * D_R Z D_C (Dimuon) or Z (Muon); o_out = O;
+// W = W - lr * (scale * O + wd * W).  Tile: 64 x 64 of the original m x n.
+// Z is read in the original orientation: the last combine wrote a tall
+// matrix's Z transposed (n x m, ld KP).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_update(StepArgs a, const Tile* __restrict__ tiles) {
+  const Tile t = tiles[blockIdx.x];
+  const MatDesc& d = a.desc[t.mat];
+  const int m = d.m, n = d.n;
+  const int tid = threadIdx.x;
+  const int r = tid >> 2, c0 = (tid & 3) * 16;
+  const int row = t.ti * 64 + r;
+  if (row >= m) return;
+  const float* z = reinterpret_cast<const float*>(a.ws + d.z_off);
+  const int64_t zld = d.tall ? d.KP : d.NP;
+  const MatScal sc = a.scal[d.scal_idx];
+  const float* dr = reinterpret_cast<const float*>(a.ws + d.dr_off);
+  const float* dc = reinterpret_cast<const float*>(a.ws + d.dc_off);
+  const float rf = a.dimuon ? dr[row] : 1.0f;
+  const int64_t off = static_cast<int64_t>(row) * n;
+  for (int h = 0; h < 2; ++h) {
+    const int col0 = t.tj * 64 + c0 + 8 * h;
+    if (col0 >= n) break;
+    float w[8], o[8];
+    load8(d.w, a.w_dt, off, col0, n, w);
+    const float4* zq = reinterpret_cast<const float4*>(z + static_cast<int64_t>(row) * zld + col0);
+    const float4 z0 = zq[0], z1 = zq[1];
+    const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int col = col0 + e;
+      if (a.dimuon) {
+        const float cf = (col < n) ? dc[col] : 1.0f;
+        o[e] = sc.post * ((rf * zv[e]) * cf);
+      } else {
+        o[e] = zv[e];
+      }
+      const float upd = d.update_scale * o[e] + a.weight_decay * w[e];
+      w[e] = w[e] - a.lr * upd;
+    }
+    store8(d.w, a.w_dt, off, col0, n, w);
+    if (d.o_out) store8(d.o_out, DT_F32, off, col0, n, o);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_momentum(const StepArgs& a, const Tile* tiles, int n, bool energies, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_momentum, dim3(n), dim3(256), 0, s, a, tiles, energies ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_condition(const StepArgs& a, const uint16_t* mats, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_condition, dim3(n), dim3(256), 0, s, a, mats);
+  return hipGetLastError();
+}
+
+hipError_t launch_prescale(const StepArgs& a, const Tile* tiles, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_prescale, dim3(n), dim3(256), 0, s, a, tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_finalize(const StepArgs& a, const uint16_t* mats, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_norm_finalize, dim3(n), dim3(256), 0, s, a, mats);
+  return hipGetLastError();
+}
+
+hipError_t launch_post_finalize(const StepArgs& a, const uint16_t* mats, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_post_finalize, dim3(n), dim3(256), 0, s, a, mats);
+  return hipGetLastError();
+}
+
+hipError_t launch_update(const StepArgs& a, const Tile* tiles, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_update, dim3(n), dim3(256), 0, s, a, tiles);
+  return hipGetLastError();
+}
+
+}  // namespace muon

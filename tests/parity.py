@@ -1,0 +1,111 @@
+"""Shared helpers of the parity tests: run a workload through the C ABI and
+through the float64 oracle on the same inputs, and compare."""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+import oracle as O
+
+# Tolerances: bf16 NS products -> max |O_gpu - O_ref| <= 2e-2 at the
+# orthogonaliser's output scale; fp32 NS -> ||O_gpu - O_ref||_F <= 1e-5 ||O_ref||_F.
+TOL_BF16_MAXABS = 2e-2
+TOL_F32_REL = 1e-5
+
+
+def f32(x: float) -> float:
+    """The float32 value the library receives for a config scalar."""
+    return float(np.float32(x))
+
+
+def ulp(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of the dtype's values at |x| (the smallest subnormal spacing at 0)."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    mant = 7 if dtype == "bf16" else 23
+    e = np.floor(np.log2(np.where(x > 0, x, 1.0)))
+    e = np.maximum(e, -126)
+    return np.where(x > 0, 2.0 ** (e - mant), 2.0 ** (-126 - mant))
+
+
+def to64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+@dataclass
+class GpuResult:
+    w: List[np.ndarray]
+    m: List[np.ndarray]
+    o: List[np.ndarray]
+    e: List[np.ndarray]
+
+
+def run_gpu(wl, variant: str, cfg, *, device="cuda", scales=None, want_energy=True) -> GpuResult:
+    """Copy the workload to the GPU, run one step through the C ABI, return float64 copies."""
+    import dimuon_newton_schulz_amd as D
+
+    params = []
+    for i, mt in enumerate(wl.mats):
+        w = mt.w.to(device).clone()
+        g = mt.g.to(device).clone()
+        mom = mt.m_prev.to(device).clone()
+        m, n = w.shape
+        params.append(D.Param(w=w, g=g, mom=mom,
+                              o_out=torch.full((m, n), float("nan"), dtype=torch.float32, device=device),
+                              energy_out=(torch.full((m + n,), float("nan"), dtype=torch.float32, device=device)
+                                          if want_energy else None),
+                              update_scale=1.0 if scales is None else scales[i]))
+    fn = D.dimuon_step if variant == "dimuon" else D.muon_step
+    fn(params, cfg)
+    torch.cuda.synchronize()
+    return GpuResult(w=[to64(p.w) for p in params], m=[to64(p.mom) for p in params],
+                     o=[to64(p.o_out) for p in params],
+                     e=[p.energy_out.cpu().numpy() if p.energy_out is not None else None for p in params])
+
+
+def run_oracle(wl, variant: str, cfg, index: int, scale: float = 1.0):
+    mt = wl.mats[index]
+    fn = O.dimuon_step if variant == "dimuon" else O.muon_step
+    kw = dict(lr=f32(cfg.lr), mu=f32(cfg.momentum), steps=cfg.ns_steps,
+              mom_dtype=cfg.mom_dtype, w_dtype=cfg.w_dtype, nesterov=cfg.nesterov,
+              weight_decay=f32(cfg.weight_decay), scale=f32(scale))
+    if cfg.coeff_schedule is not None:
+        kw["schedule"] = [tuple(f32(v) for v in row) for row in cfg.coeff_schedule]
+    else:
+        kw["coeffs"] = (f32(cfg.a), f32(cfg.b), f32(cfg.c))
+    if variant == "dimuon":
+        kw["eps"] = f32(cfg.dimuon_eps)
+    return fn(to64(mt.w), to64(mt.g), to64(mt.m_prev), **kw)
+
+
+def check_matrix(gpu: GpuResult, ref, i: int, cfg, variant: str, wl, scale: float = 1.0,
+                 o_tol: Optional[float] = None):
+    """Element-by-element comparison of matrix i; raises AssertionError with context."""
+    ctx = f"matrix {i} shape {wl.mats[i].shape} ({variant}, ns {cfg.ns_dtype})"
+    o_g, o_r = gpu.o[i], ref.o
+    assert np.all(np.isfinite(o_g)), f"{ctx}: non-finite O"
+    if cfg.ns_dtype == "bf16":
+        err = np.max(np.abs(o_g - o_r))
+        tol = TOL_BF16_MAXABS if o_tol is None else o_tol
+        assert err <= tol, f"{ctx}: max|dO| = {err:.3e} > {tol}"
+    else:
+        err = np.linalg.norm(o_g - o_r) / max(np.linalg.norm(o_r), 1e-300)
+        tol = TOL_F32_REL if o_tol is None else o_tol
+        assert err <= tol, f"{ctx}: rel ||dO|| = {err:.3e} > {tol}"
+    # Momentum: within 1 ulp of its dtype.
+    dm = np.abs(gpu.m[i] - ref.m)
+    assert np.all(dm <= ulp(ref.m, cfg.mom_dtype)), f"{ctx}: momentum off by more than 1 ulp ({dm.max():.3e})"
+    # Weights: the update applied to the GPU's own O, within 1 ulp of the W dtype.
+    w0 = to64(wl.mats[i].w)
+    w_ref = w0 - f32(cfg.lr) * (f32(scale) * o_g + f32(cfg.weight_decay) * w0)
+    dw = np.abs(gpu.w[i] - w_ref)
+    assert np.all(dw <= ulp(w_ref, cfg.w_dtype) + 1e-30), f"{ctx}: W off by more than 1 ulp ({dw.max():.3e})"
+    # Energies: bit-exact against the oracle's float32 tree.
+    if variant == "dimuon" and gpu.e[i] is not None:
+        m, n = wl.mats[i].shape
+        np.testing.assert_array_equal(gpu.e[i][:m], ref.r, err_msg=f"{ctx}: row energies")
+        np.testing.assert_array_equal(gpu.e[i][m:], ref.c, err_msg=f"{ctx}: column energies")
+    return err

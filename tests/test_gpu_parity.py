@@ -1,0 +1,175 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Each case prints its name, shapes and variant before touching the GPU.
+Inputs come from the seeded generators in ``workloads``; expected values
+come only from ``oracle``."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import dimuon_newton_schulz_amd as D
+import workloads as W
+from parity import check_matrix, f32, run_gpu, run_oracle, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def cfg_of(wl, **kw):
+    base = dict(lr=wl.lr, momentum=wl.mu, ns_steps=wl.ns_steps, w_dtype=wl.w_dtype, g_dtype=wl.g_dtype,
+                mom_dtype=wl.mom_dtype, ns_dtype=wl.ns_dtype)
+    base.update(kw)
+    return D.StepConfig(**base)
+
+
+def run_case(wl, variant, cfg, indices=None, scales=None, o_tol=None):
+    announce(f"{wl.name} {variant} ns={cfg.ns_dtype} count={wl.count} "
+             f"shapes={sorted(set(m.shape for m in wl.mats))}")
+    gpu = run_gpu(wl, variant, cfg, scales=scales)
+    idx = range(wl.count) if indices is None else indices
+    errs = []
+    for i in idx:
+        ref = run_oracle(wl, variant, cfg, i, 1.0 if scales is None else scales[i])
+        errs.append(check_matrix(gpu, ref, i, cfg, variant, wl, 1.0 if scales is None else scales[i], o_tol))
+    return gpu, errs
+
+
+# ---------------------------------------------------------------------------
+# Thin path (Gram side <= 32): one kernel per batch
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
+def test_lora_toy_4x16_f32(variant):
+    wl = W.lora_toy(seed=0)
+    run_case(wl, variant, cfg_of(wl))
+
+
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
+@pytest.mark.parametrize("ns", ["bf16", "f32"])
+def test_lora_batch_small(variant, ns):
+    wl = W.lora_batch(pairs=6, rank=8, d=4096, seed=1)
+    run_case(wl, variant, cfg_of(wl, ns_dtype=ns))
+
+
+@pytest.mark.parametrize("shape", [(1, 40), (40, 1), (3, 1000), (1000, 3), (5, 333), (16, 2048), (2048, 16),
+                                   (32, 1024), (1024, 32), (2, 9000), (9000, 2), (7, 4093)])
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
+def test_thin_ragged_shapes(shape, variant):
+    for dt in ("f32", "bf16"):
+        wl = W.random_batch([shape], dtype=dt, ns_dtype="f32", seed=hash(shape) % 97, variant=variant)
+        run_case(wl, variant, cfg_of(wl))
+
+
+# ---------------------------------------------------------------------------
+# General path (bf16 MFMA and fp32 GEMMs)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
+@pytest.mark.parametrize("ns", ["bf16", "f32"])
+def test_general_ragged_mixed_batch(variant, ns):
+    shapes = [(300, 700), (700, 300), (256, 256), (130, 1000), (1000, 130), (33, 500), (129, 129)]
+    wl = W.random_batch(shapes, dtype="bf16", ns_dtype=ns, seed=3, variant=variant)
+    run_case(wl, variant, cfg_of(wl))
+
+
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
+def test_general_f32_storage(variant):
+    shapes = [(200, 333), (333, 200), (64, 1024)]
+    wl = W.random_batch(shapes, dtype="f32", ns_dtype="f32", seed=4, variant=variant)
+    run_case(wl, variant, cfg_of(wl))
+
+
+def test_gpt2_shapes_scaled():
+    wl = W.gpt2_hidden(layers=1, d_model=256, seed=5)
+    run_case(wl, "muon", cfg_of(wl))
+
+
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
+def test_square_spectrum_scaled(variant):
+    wl = W.square_batch(count=2, n=512, seed=6, variant=variant)
+    run_case(wl, variant, cfg_of(wl))
+
+
+def test_moe_scaled_zero_rows():
+    wl = W.moe_experts(experts=2, d_model=384, d_ff=264, seed=7)
+    gpu, _ = run_case(wl, "dimuon", cfg_of(wl))
+
+
+# ---------------------------------------------------------------------------
+# Method properties on the GPU
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shapes", [[(8, 4096), (4096, 8), (4, 16)], [(300, 700), (700, 300), (256, 256)]])
+def test_first_step_dimuon_equals_muon_bitwise(shapes):
+    wl = W.random_batch(shapes, dtype="bf16", ns_dtype="bf16", seed=8, zero_prev=True)
+    cfg = cfg_of(wl)
+    announce(f"first-step identity {shapes}")
+    a = run_gpu(wl, "muon", cfg)
+    b = run_gpu(wl, "dimuon", cfg)
+    for i in range(wl.count):
+        np.testing.assert_array_equal(a.o[i], b.o[i])
+        np.testing.assert_array_equal(a.w[i], b.w[i])
+        np.testing.assert_array_equal(a.m[i], b.m[i])
+        m, n = wl.mats[i].shape
+        assert np.all(b.e[i] == 0)
+
+
+def test_extensions_nesterov_decay_schedule_scale():
+    shapes = [(8, 1024), (1024, 8), (200, 300), (300, 200)]
+    sched = [(4.0, -5.0, 2.0), (3.5, -4.5, 1.9), (3.0, -3.2, 1.2), (2.5, -2.0, 0.6), (1.9, -1.3, 0.4)]
+    scales = [0.5, 2.0, 1.5, 0.25]
+    for variant in ("muon", "dimuon"):
+        wl = W.random_batch(shapes, dtype="bf16", ns_dtype="bf16", seed=9, variant=variant)
+        cfg = cfg_of(wl, nesterov=True, weight_decay=0.1, coeff_schedule=sched)
+        run_case(wl, variant, cfg, scales=scales)
+
+
+@pytest.mark.parametrize("steps", [0, 1, 7])
+def test_other_iteration_counts(steps):
+    shapes = [(8, 512), (160, 300)]
+    wl = W.random_batch(shapes, dtype="bf16", ns_dtype="bf16", seed=10)
+    run_case(wl, "muon", cfg_of(wl, ns_steps=steps))
+
+
+def test_zero_gradient_and_momentum_gives_zero_step():
+    wl = W.random_batch([(8, 256), (130, 260)], dtype="bf16", ns_dtype="bf16", seed=11, zero_prev=True,
+                        grad_std=0.0)
+    for variant in ("muon", "dimuon"):
+        gpu = run_gpu(wl, variant, cfg_of(wl))
+        for i in range(wl.count):
+            assert np.all(gpu.o[i] == 0)
+            np.testing.assert_array_equal(gpu.w[i], to64(wl.mats[i].w))
+
+
+def test_repeated_steps_track_oracle():
+    # Three consecutive steps with fresh gradients; momentum carried on device.
+    shapes = [(8, 2048), (256, 384)]
+    wl = W.random_batch(shapes, dtype="f32", ns_dtype="f32", seed=12, variant="dimuon")
+    cfg = cfg_of(wl)
+    import oracle as O
+    params = [D.Param(w=m.w.cuda().clone(), g=m.g.cuda().clone(), mom=m.m_prev.cuda().clone(),
+                      o_out=torch.empty(m.shape, device="cuda")) for m in wl.mats]
+    ws = D.workspace_for(params, cfg)
+    ref_w = [to64(m.w) for m in wl.mats]
+    ref_m = [to64(m.m_prev) for m in wl.mats]
+    for step in range(3):
+        grads = W.random_batch(shapes, dtype="f32", seed=100 + step)
+        for p, gm in zip(params, grads.mats):
+            p.g.copy_(gm.g.cuda())
+        announce(f"repeated step {step}")
+        D.dimuon_step(params, cfg, workspace=ws)
+        torch.cuda.synchronize()
+        for i, p in enumerate(params):
+            r = O.dimuon_step(ref_w[i], to64(grads.mats[i].g), ref_m[i], lr=f32(cfg.lr), mu=f32(cfg.momentum),
+                              mom_dtype="f32", w_dtype="f32", eps=f32(cfg.dimuon_eps))
+            o = to64(p.o_out)
+            rel = np.linalg.norm(o - r.o) / np.linalg.norm(r.o)
+            assert rel < 1e-5, (step, i, rel)
+            ref_w[i], ref_m[i] = to64(p.w), to64(p.mom)   # follow the GPU state
