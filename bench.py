@@ -80,11 +80,14 @@ def algorithmic(wl, is_thin):
 
 
 def is_thin(m, n):
+    """Same rule as the library's planner: Gram side <= 32 and the long side
+    within the single-workgroup kernel's capacity."""
     k, big = min(m, n), max(m, n)
     p = 1
     while p < k:
         p *= 2
-    return k <= 32 and p * big <= 32768
+    cap = 32 if p <= 2 else 64
+    return k <= 32 and big <= 512 * cap // p
 
 
 def measure(wl, steps, warmup, sets, ns_dtype=None):
@@ -93,24 +96,22 @@ def measure(wl, steps, warmup, sets, ns_dtype=None):
 
     cfg = D.StepConfig(lr=wl.lr, momentum=wl.mu, ns_steps=wl.ns_steps, w_dtype=wl.w_dtype,
                        g_dtype=wl.g_dtype, mom_dtype=wl.mom_dtype, ns_dtype=ns_dtype or wl.ns_dtype)
-    step_fn = D.dimuon_step if wl.variant == "dimuon" else D.muon_step
-    batches = []
+    dimuon = wl.variant == "dimuon"
+    plans = []
     for s in range(sets):
         params = [D.Param(w=m.w.clone() if s else m.w, g=m.g.clone() if s else m.g,
                           mom=m.m_prev.clone() if s else m.m_prev) for m in wl.mats]
-        batches.append((params, D.workspace_for(params, cfg)))
+        plans.append(D.Plan(params, cfg, dimuon=dimuon))
     torch.cuda.synchronize()
     for i in range(warmup):
-        p, ws = batches[i % sets]
-        step_fn(p, cfg, workspace=ws)
+        plans[i % sets].step()
     torch.cuda.synchronize()
 
     # Timed region: K steps, HIP events around it on the library's stream.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(steps):
-        p, ws = batches[i % sets]
-        step_fn(p, cfg, workspace=ws)
+        plans[i % sets].step()
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
@@ -130,12 +131,11 @@ def measure(wl, steps, warmup, sets, ns_dtype=None):
     counts = []
     hs = ctypes.sizeof(ctypes.c_void_p)
     for i in range(steps):
-        p, ws = batches[i % sets]
         base = i * per_step
         lib.muon_set_launch_events(ctypes.cast(ctypes.addressof(handles) + base * hs, ctypes.c_void_p),
                                    ctypes.cast(ctypes.addressof(kinds) + base * 4,
                                                ctypes.POINTER(ctypes.c_int32)), per_step)
-        step_fn(p, cfg, workspace=ws)
+        plans[i % sets].step()
         counts.append(lib.muon_set_launch_events(None, None, 0))
     torch.cuda.synchronize()
     per_kind = {}
@@ -146,7 +146,9 @@ def measure(wl, steps, warmup, sets, ns_dtype=None):
             dt = events[base + j - 1].elapsed_time(events[base + j])
             tot, n = per_kind.get(kind, (0.0, 0))
             per_kind[kind] = (tot + dt, n + 1)
-    del batches
+    for p in plans:
+        p.close()
+    del plans
     torch.cuda.empty_cache()
     return cfg, ms, per_kind
 

@@ -30,8 +30,8 @@ STATUS_NAMES = {0: "MUON_OK", 1: "MUON_ERR_INVALID_ARG", 2: "MUON_ERR_DTYPE",
                 6: "MUON_ERR_UNSUPPORTED"}
 
 EXPORTED_SYMBOLS = ("muon_config_default", "muon_workspace_bytes", "muon_step", "dimuon_step",
-                    "muon_set_launch_events", "muon_workspace_invalidate", "muon_status_string",
-                    "muon_last_error", "muon_abi_version")
+                    "muon_set_launch_events", "muon_plan_create", "muon_plan_step", "muon_plan_set_lr",
+                    "muon_plan_destroy", "muon_status_string", "muon_last_error", "muon_abi_version")
 
 LAUNCH_KINDS = {-1: "start", 0: "thin", 1: "momentum", 2: "condition", 3: "prescale", 4: "norm",
                 5: "gram", 6: "poly", 7: "combine", 8: "postnorm", 9: "update"}
@@ -84,8 +84,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.muon_set_launch_events.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]
     lib.muon_set_launch_events.restype = ctypes.c_int32
-    lib.muon_workspace_invalidate.argtypes = [ctypes.c_void_p]
-    lib.muon_workspace_invalidate.restype = None
+    lib.muon_plan_create.argtypes = [ctypes.POINTER(MuonMatrix), ctypes.c_int64, ctypes.POINTER(MuonConfig),
+                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                     ctypes.POINTER(ctypes.c_void_p)]
+    lib.muon_plan_create.restype = ctypes.c_int
+    lib.muon_plan_step.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.muon_plan_step.restype = ctypes.c_int
+    lib.muon_plan_set_lr.argtypes = [ctypes.c_void_p, ctypes.c_float]
+    lib.muon_plan_set_lr.restype = ctypes.c_int
+    lib.muon_plan_destroy.argtypes = [ctypes.c_void_p]
+    lib.muon_plan_destroy.restype = None
     lib.muon_status_string.argtypes = [ctypes.c_int]
     lib.muon_status_string.restype = ctypes.c_char_p
     lib.muon_last_error.argtypes = []
@@ -221,9 +229,7 @@ def _step(fn_name: str, params: Sequence[Param], cfg: StepConfig, workspace: Opt
     c, _keep = cfg.to_c()
     if workspace is None:
         workspace = workspace_for(params, cfg)
-    if stream is None:
-        stream = torch.cuda.current_stream(params[0].w.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    handle = _stream_handle(stream, params[0].w.device)
     fn = getattr(lib, fn_name)
     with torch.cuda.device(params[0].w.device):
         _check(fn(arr, len(params), ctypes.byref(c), ctypes.c_void_p(workspace.data_ptr()),
@@ -278,11 +284,55 @@ class LaunchTimer:
         return n
 
 
-def muon_workspace_invalidate(workspace: torch.Tensor):
-    load_library().muon_workspace_invalidate(ctypes.c_void_p(workspace.data_ptr()))
+def _stream_handle(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class Plan:
+    """A prepared batch (muon_plan_t): validated and uploaded once, then
+    stepped repeatedly.  Keeps the tensors and the workspace alive."""
+
+    def __init__(self, params: Sequence[Param], cfg: StepConfig, dimuon: bool,
+                 workspace: Optional[torch.Tensor] = None, stream=None):
+        lib = load_library()
+        _check_dtypes(params, cfg)
+        self.params = list(params)
+        self.cfg = cfg
+        self.device = params[0].w.device
+        self.workspace = workspace if workspace is not None else workspace_for(params, cfg)
+        arr = _marshal(params)
+        c, keep = cfg.to_c()
+        handle = ctypes.c_void_p(0)
+        with torch.cuda.device(self.device):
+            _check(lib.muon_plan_create(arr, len(params), ctypes.byref(c), 1 if dimuon else 0,
+                                        ctypes.c_void_p(self.workspace.data_ptr()),
+                                        ctypes.c_size_t(self.workspace.numel()),
+                                        ctypes.c_void_p(_stream_handle(stream, self.device)),
+                                        ctypes.byref(handle)))
+        self._handle = handle
+        self._lib = lib
+
+    def step(self, stream=None):
+        _check(self._lib.muon_plan_step(self._handle, ctypes.c_void_p(_stream_handle(stream, self.device))))
+
+    def set_lr(self, lr: float):
+        _check(self._lib.muon_plan_set_lr(self._handle, lr))
+
+    def close(self):
+        if self._handle:
+            self._lib.muon_plan_destroy(self._handle)
+            self._handle = ctypes.c_void_p(0)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 __all__ = ["MuonMatrix", "MuonConfig", "MuonError", "StepConfig", "Param", "load_library",
            "muon_step", "dimuon_step", "muon_workspace_bytes", "muon_status_string",
-           "muon_workspace_invalidate", "workspace_for", "config_for", "EXPORTED_SYMBOLS", "LaunchTimer",
+           "Plan", "workspace_for", "config_for", "EXPORTED_SYMBOLS", "LaunchTimer",
            "LAUNCH_KINDS"]

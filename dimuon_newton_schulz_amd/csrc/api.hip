@@ -49,7 +49,6 @@ muon_status_t fail(muon_status_t st, const char* fmt, ...) {
 
 constexpr int64_t kMaxDim = 65536;
 constexpr int kThinMaxK = 32;
-constexpr int64_t kThinMaxElems = 32768;   // KP * N held on chip by one workgroup
 constexpr size_t kAlign = 256;
 
 inline int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -80,9 +79,14 @@ struct Plan {
   std::vector<unsigned char> table;
 };
 
+// The thin kernel holds CAP floats of the matrix per thread (512 threads):
+// CAP = 32 for a padded Gram side KP <= 2, else 64, so N <= 512 * CAP / KP.
 bool is_thin(int64_t m, int64_t n) {
   const int64_t k = std::min(m, n), N = std::max(m, n);
-  return k <= kThinMaxK && static_cast<int64_t>(next_pow2(k)) * N <= kThinMaxElems;
+  if (k > kThinMaxK) return false;
+  const int64_t kp = next_pow2(k);
+  const int64_t cap = kp <= 2 ? 32 : 64;
+  return N <= 512 * cap / kp;
 }
 
 muon_status_t validate_config(const muon_config_t* cfg) {
@@ -270,64 +274,127 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
 }
 
 // ---------------------------------------------------------------------------
-// Descriptor upload cache, keyed by workspace address
+// Descriptor upload: the table is copied from a pinned host buffer into the
+// workspace prefix on the step's stream.  An event records when the copy has
+// consumed the host buffer, so the buffer is never overwritten early.
 // ---------------------------------------------------------------------------
-struct CacheEntry {
-  std::vector<unsigned char> table;   // what the workspace prefix holds
-  void* pinned = nullptr;
+struct Staging {
+  void* host = nullptr;
   size_t cap = 0;
   hipEvent_t ev = nullptr;
-  bool ev_pending = false;
-};
+  bool pending = false;
 
-std::mutex g_cache_mu;
-std::map<uintptr_t, CacheEntry> g_cache;
-
-muon_status_t upload_table(const Plan& p, void* ws, hipStream_t stream) {
-  std::lock_guard<std::mutex> lock(g_cache_mu);
-  CacheEntry& e = g_cache[reinterpret_cast<uintptr_t>(ws)];
-  if (e.table == p.table) return MUON_OK;
-  hipError_t err;
-  if (e.ev_pending) {
-    if ((err = hipEventSynchronize(e.ev)) != hipSuccess)
-      return fail(MUON_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(err));
-    e.ev_pending = false;
-  }
-  if (e.cap < p.table.size()) {
-    if (e.pinned) (void)hipHostFree(e.pinned);
-    e.pinned = nullptr;
-    e.cap = 0;
-    if ((err = hipHostMalloc(&e.pinned, p.table.size(), hipHostMallocDefault)) != hipSuccess) {
-      e.pinned = nullptr;
-      e.table.clear();
-      return fail(MUON_ERR_HIP, "hipHostMalloc(%zu): %s", p.table.size(), hipGetErrorString(err));
+  muon_status_t upload(const std::vector<unsigned char>& table, void* dst, hipStream_t s) {
+    hipError_t err;
+    if (pending) {
+      if ((err = hipEventSynchronize(ev)) != hipSuccess)
+        return fail(MUON_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(err));
+      pending = false;
     }
-    e.cap = p.table.size();
-  }
-  if (!e.ev) {
-    if ((err = hipEventCreateWithFlags(&e.ev, hipEventDisableTiming)) != hipSuccess) {
-      e.ev = nullptr;
-      e.table.clear();
+    if (cap < table.size()) {
+      if (host) (void)hipHostFree(host);
+      host = nullptr;
+      cap = 0;
+      if ((err = hipHostMalloc(&host, table.size(), hipHostMallocDefault)) != hipSuccess) {
+        host = nullptr;
+        return fail(MUON_ERR_HIP, "hipHostMalloc(%zu): %s", table.size(), hipGetErrorString(err));
+      }
+      cap = table.size();
+    }
+    if (!ev && (err = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) {
+      ev = nullptr;
       return fail(MUON_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(err));
     }
+    std::memcpy(host, table.data(), table.size());
+    if ((err = hipMemcpyAsync(dst, host, table.size(), hipMemcpyHostToDevice, s)) != hipSuccess)
+      return fail(MUON_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(err));
+    if ((err = hipEventRecord(ev, s)) != hipSuccess)
+      return fail(MUON_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(err));
+    pending = true;
+    return MUON_OK;
   }
-  std::memcpy(e.pinned, p.table.data(), p.table.size());
-  if ((err = hipMemcpyAsync(ws, e.pinned, p.table.size(), hipMemcpyHostToDevice, stream)) != hipSuccess) {
-    e.table.clear();
-    return fail(MUON_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(err));
+
+  void release() {
+    if (pending && ev) (void)hipEventSynchronize(ev);
+    if (ev) (void)hipEventDestroy(ev);
+    if (host) (void)hipHostFree(host);
+    host = nullptr;
+    ev = nullptr;
+    cap = 0;
+    pending = false;
   }
-  if ((err = hipEventRecord(e.ev, stream)) != hipSuccess) {
-    e.table.clear();
-    return fail(MUON_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(err));
+};
+
+// Stateless calls rotate through a few staging buffers per host thread, so
+// the host can run several steps ahead of the GPU.  They live until the
+// process ends.
+constexpr int kRing = 4;
+struct StagingRing {
+  Staging slot[kRing];
+  int next = 0;
+};
+thread_local StagingRing* g_ring = nullptr;
+
+// ---------------------------------------------------------------------------
+// Shared pieces of a step
+// ---------------------------------------------------------------------------
+muon_status_t prepare(const muon_matrix_t* mats, int64_t count, const muon_config_t* cfg, void* ws,
+                      size_t ws_bytes, Plan& p) {
+  muon_status_t st;
+  if ((st = validate_config(cfg)) != MUON_OK) return st;
+  if ((st = validate_shapes(mats, count)) != MUON_OK) return st;
+  if ((st = validate_buffers(mats, count, cfg)) != MUON_OK) return st;
+  if ((st = build_plan(mats, count, cfg, true, p)) != MUON_OK) return st;
+  if (!ws) return fail(MUON_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return fail(MUON_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (ws_bytes < p.total_bytes)
+    return fail(MUON_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, p.total_bytes);
+  // The workspace must not overlap any caller buffer.
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(ws), hi = lo + p.total_bytes;
+  for (int64_t i = 0; i < count; ++i) {
+    const muon_matrix_t& x = mats[i];
+    const size_t elems = static_cast<size_t>(x.m) * x.n;
+    const void* ps[5] = {x.w, x.g, x.mom, x.o_out, x.energy_out};
+    const size_t bytes[5] = {elems * dtype_size(cfg->w_dtype), elems * dtype_size(cfg->g_dtype),
+                             elems * dtype_size(cfg->mom_dtype), elems * 4, static_cast<size_t>(x.m + x.n) * 4};
+    for (int b = 0; b < 5; ++b) {
+      if (!ps[b]) continue;
+      const uintptr_t plo = reinterpret_cast<uintptr_t>(ps[b]);
+      if (plo < hi && lo < plo + bytes[b])
+        return fail(MUON_ERR_ALIAS, "matrix %lld buffer %d overlaps the workspace", (long long)i, b);
+    }
   }
-  e.ev_pending = true;
-  e.table = p.table;
   return MUON_OK;
 }
 
-// ---------------------------------------------------------------------------
-// One step
-// ---------------------------------------------------------------------------
+StepArgs make_args(const Plan& p, const muon_config_t& cfg, void* ws, bool dimuon) {
+  char* base = static_cast<char*>(ws);
+  StepArgs a{};
+  a.desc = reinterpret_cast<const MatDesc*>(base + p.desc_off);
+  a.scal = reinterpret_cast<MatScal*>(base + p.scal_off);
+  a.ws = base;
+  a.mu = cfg.momentum;
+  a.lr = cfg.lr;
+  a.eps = cfg.dimuon_eps;
+  a.weight_decay = cfg.weight_decay;
+  a.g_dt = cfg.g_dtype;
+  a.mom_dt = cfg.mom_dtype;
+  a.w_dt = cfg.w_dtype;
+  a.ns_dt = cfg.ns_dtype;
+  a.nesterov = cfg.nesterov ? 1 : 0;
+  a.dimuon = dimuon ? 1 : 0;
+  return a;
+}
+
+void make_coeffs(const muon_config_t& cfg, Coeffs* cf) {
+  for (int t = 0; t < cfg.ns_steps; ++t) {
+    if (cfg.coeff_schedule)
+      cf[t] = {cfg.coeff_schedule[3 * t], cfg.coeff_schedule[3 * t + 1], cfg.coeff_schedule[3 * t + 2]};
+    else
+      cf[t] = {cfg.a, cfg.b, cfg.c};
+  }
+}
+
 #define MUON_HIP_TRY(expr)                                                                 \
   do {                                                                                     \
     hipError_t e_ = (expr);                                                                \
@@ -341,74 +408,18 @@ muon_status_t upload_table(const Plan& p, void* ws, hipStream_t stream) {
     MUON_HIP_TRY(hook_record((kind), s));    \
   } while (0)
 
-muon_status_t run_step(const muon_matrix_t* mats, int64_t count, const muon_config_t* cfg, void* ws,
-                       size_t ws_bytes, void* stream_ptr, bool dimuon) {
-  g_last_error.clear();
-  muon_status_t st;
-  if ((st = validate_config(cfg)) != MUON_OK) return st;
-  if ((st = validate_shapes(mats, count)) != MUON_OK) return st;
-  if ((st = validate_buffers(mats, count, cfg)) != MUON_OK) return st;
-  Plan p;
-  if ((st = build_plan(mats, count, cfg, true, p)) != MUON_OK) return st;
-  if (!ws) return fail(MUON_ERR_WORKSPACE, "workspace is NULL");
-  if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return fail(MUON_ERR_WORKSPACE, "workspace not 256-byte aligned");
-  if (ws_bytes < p.total_bytes)
-    return fail(MUON_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, p.total_bytes);
-  // The workspace must not overlap any caller buffer.
-  {
-    const uintptr_t lo = reinterpret_cast<uintptr_t>(ws), hi = lo + p.total_bytes;
-    for (int64_t i = 0; i < count; ++i) {
-      const muon_matrix_t& x = mats[i];
-      const size_t elems = static_cast<size_t>(x.m) * x.n;
-      const void* ps[5] = {x.w, x.g, x.mom, x.o_out, x.energy_out};
-      const size_t bytes[5] = {elems * dtype_size(cfg->w_dtype), elems * dtype_size(cfg->g_dtype),
-                               elems * dtype_size(cfg->mom_dtype), elems * 4,
-                               static_cast<size_t>(x.m + x.n) * 4};
-      for (int b = 0; b < 5; ++b) {
-        if (!ps[b]) continue;
-        const uintptr_t plo = reinterpret_cast<uintptr_t>(ps[b]);
-        if (plo < hi && lo < plo + bytes[b])
-          return fail(MUON_ERR_ALIAS, "matrix %lld buffer %d overlaps the workspace", (long long)i, b);
-      }
-    }
-  }
-
-  hipStream_t s = static_cast<hipStream_t>(stream_ptr);
-  if ((st = upload_table(p, ws, s)) != MUON_OK) return st;
-
-  char* base = static_cast<char*>(ws);
-  StepArgs a{};
-  a.desc = reinterpret_cast<const MatDesc*>(base + p.desc_off);
-  a.scal = reinterpret_cast<MatScal*>(base + p.scal_off);
-  a.ws = base;
-  a.mu = cfg->momentum;
-  a.lr = cfg->lr;
-  a.eps = cfg->dimuon_eps;
-  a.weight_decay = cfg->weight_decay;
-  a.g_dt = cfg->g_dtype;
-  a.mom_dt = cfg->mom_dtype;
-  a.w_dt = cfg->w_dtype;
-  a.ns_dt = cfg->ns_dtype;
-  a.nesterov = cfg->nesterov ? 1 : 0;
-  a.dimuon = dimuon ? 1 : 0;
-
-  Coeffs cf[kMaxSteps];
-  for (int t = 0; t < cfg->ns_steps; ++t) {
-    if (cfg->coeff_schedule)
-      cf[t] = {cfg->coeff_schedule[3 * t], cfg->coeff_schedule[3 * t + 1], cfg->coeff_schedule[3 * t + 2]};
-    else
-      cf[t] = {cfg->a, cfg->b, cfg->c};
-  }
-
+// The launch sequence of one step; the descriptor table is already on the
+// device (ordered before these launches on stream s).
+muon_status_t launch_all(const Plan& p, const StepArgs& a, const Coeffs* cf, int ns_steps, bool dimuon,
+                         hipStream_t s) {
+  char* base = a.ws;
   auto tl = [&](size_t off) { return reinterpret_cast<const Tile*>(base + off); };
   auto il = [&](size_t off) { return reinterpret_cast<const uint16_t*>(base + off); };
-
   g_hook.next = 0;
   MUON_HIP_TRY(hook_record(MUON_LAUNCH_START, s));
   for (const auto& g : p.thin)
     MUON_LAUNCH(MUON_LAUNCH_THIN,
-                launch_thin(a, il(g.off), static_cast<int>(g.ids.size()), g.kp, g.tall, cfg->ns_steps, cf, s));
-
+                launch_thin(a, il(g.off), static_cast<int>(g.ids.size()), g.kp, g.tall, ns_steps, cf, s));
   if (!p.gen.empty()) {
     const int ng = static_cast<int>(p.gen.size());
     MUON_LAUNCH(MUON_LAUNCH_MOMENTUM, launch_momentum(a, tl(p.k1_off), static_cast<int>(p.k1.size()), dimuon, s));
@@ -416,13 +427,12 @@ muon_status_t run_step(const muon_matrix_t* mats, int64_t count, const muon_conf
     MUON_LAUNCH(MUON_LAUNCH_PRESCALE, launch_prescale(a, tl(p.k3_off), static_cast<int>(p.k3.size()), s));
     MUON_LAUNCH(MUON_LAUNCH_NORM, launch_norm_finalize(a, il(p.gen_off), ng, s));
     const int nsyrk = static_cast<int>(p.syrk.size()), ncomb = static_cast<int>(p.comb.size());
-    if (cfg->ns_steps == 0) {
+    if (ns_steps == 0)
       MUON_LAUNCH(MUON_LAUNCH_COMBINE,
                   launch_combine(a, tl(p.comb_off), ncomb, 0, 1, true, true, false, Coeffs{1.0f, 0.0f, 0.0f}, s));
-    }
-    for (int t = 0; t < cfg->ns_steps; ++t) {
+    for (int t = 0; t < ns_steps; ++t) {
       const int src = t & 1, dst = src ^ 1;
-      const bool first = t == 0, last = t == cfg->ns_steps - 1;
+      const bool first = t == 0, last = t == ns_steps - 1;
       MUON_LAUNCH(MUON_LAUNCH_GRAM, launch_syrk(a, tl(p.syrk_off), nsyrk, 0, src, first, cf[t], s));
       MUON_LAUNCH(MUON_LAUNCH_POLY, launch_syrk(a, tl(p.syrk_off), nsyrk, 1, src, first, cf[t], s));
       MUON_LAUNCH(MUON_LAUNCH_COMBINE, launch_combine(a, tl(p.comb_off), ncomb, src, dst, first, last, true, cf[t], s));
@@ -434,8 +444,35 @@ muon_status_t run_step(const muon_matrix_t* mats, int64_t count, const muon_conf
   return MUON_OK;
 }
 
+muon_status_t run_step(const muon_matrix_t* mats, int64_t count, const muon_config_t* cfg, void* ws,
+                       size_t ws_bytes, void* stream_ptr, bool dimuon) {
+  g_last_error.clear();
+  Plan p;
+  muon_status_t st = prepare(mats, count, cfg, ws, ws_bytes, p);
+  if (st != MUON_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream_ptr);
+  if (!g_ring) g_ring = new StagingRing();
+  Staging& slot = g_ring->slot[g_ring->next];
+  g_ring->next = (g_ring->next + 1) % kRing;
+  if ((st = slot.upload(p.table, ws, s)) != MUON_OK) return st;
+  Coeffs cf[kMaxSteps];
+  make_coeffs(*cfg, cf);
+  return launch_all(p, make_args(p, *cfg, ws, dimuon), cf, cfg->ns_steps, dimuon, s);
+}
+
 }  // namespace
 }  // namespace muon
+
+// A prepared batch: validated, planned and uploaded once.
+struct muon_plan {
+  muon::Plan p;
+  muon_config_t cfg;
+  std::vector<float> schedule;
+  muon::Coeffs cf[muon::kMaxSteps];
+  bool dimuon;
+  void* ws;
+  muon::Staging staging;
+};
 
 // ---------------------------------------------------------------------------
 // C ABI
@@ -494,10 +531,52 @@ int32_t muon_set_launch_events(void* const* events, int32_t* kinds, int32_t n) {
   return last;
 }
 
-void muon_workspace_invalidate(void* workspace) {
-  std::lock_guard<std::mutex> lock(muon::g_cache_mu);
-  auto it = muon::g_cache.find(reinterpret_cast<uintptr_t>(workspace));
-  if (it != muon::g_cache.end()) it->second.table.clear();
+muon_status_t muon_plan_create(const muon_matrix_t* mats, int64_t count, const muon_config_t* cfg, int32_t dimuon,
+                               void* workspace, size_t workspace_bytes, void* stream, muon_plan_t** plan) {
+  using namespace muon;
+  g_last_error.clear();
+  if (!plan) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
+  *plan = nullptr;
+  muon_plan* pl = new muon_plan();
+  muon_status_t st = prepare(mats, count, cfg, workspace, workspace_bytes, pl->p);
+  if (st == MUON_OK) st = pl->staging.upload(pl->p.table, workspace, static_cast<hipStream_t>(stream));
+  if (st != MUON_OK) {
+    pl->staging.release();
+    delete pl;
+    return st;
+  }
+  pl->cfg = *cfg;
+  if (cfg->coeff_schedule) {
+    pl->schedule.assign(cfg->coeff_schedule, cfg->coeff_schedule + 3 * cfg->ns_steps);
+    pl->cfg.coeff_schedule = pl->schedule.data();
+  }
+  make_coeffs(pl->cfg, pl->cf);
+  pl->dimuon = dimuon != 0;
+  pl->ws = workspace;
+  *plan = pl;
+  return MUON_OK;
+}
+
+muon_status_t muon_plan_step(muon_plan_t* plan, void* stream) {
+  using namespace muon;
+  g_last_error.clear();
+  if (!plan) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
+  return launch_all(plan->p, make_args(plan->p, plan->cfg, plan->ws, plan->dimuon), plan->cf, plan->cfg.ns_steps,
+                    plan->dimuon, static_cast<hipStream_t>(stream));
+}
+
+muon_status_t muon_plan_set_lr(muon_plan_t* plan, float lr) {
+  using namespace muon;
+  if (!plan) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
+  if (!finite(lr)) return fail(MUON_ERR_INVALID_ARG, "lr must be finite");
+  plan->cfg.lr = lr;
+  return MUON_OK;
+}
+
+void muon_plan_destroy(muon_plan_t* plan) {
+  if (!plan) return;
+  plan->staging.release();
+  delete plan;
 }
 
 const char* muon_status_string(muon_status_t status) {

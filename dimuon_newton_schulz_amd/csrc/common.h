@@ -109,6 +109,30 @@ __device__ __forceinline__ float round_to(float v, int32_t dt) {
   return bf16_to_f32(f32_to_bf16(v));
 }
 
+// Correctly rounded storage of a double: round to float32 with
+// round-to-odd, then to the dtype with round-to-nearest-even.  Round-to-odd
+// to 24 bits keeps enough information for the final rounding to 8 bits to
+// equal the direct rounding of d, which plain RNE-then-RNE does not.
+__device__ __forceinline__ float round_from_f64(double d, int32_t dt) {
+  float f = static_cast<float>(d);
+  if (dt == DT_F32) return f;
+  const double fd = static_cast<double>(f);
+  if (fd != d && fd == fd && d == d) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 1u) == 0u) u += (fabs(d) > fabs(fd)) ? 1u : 0xffffffffu;
+    f = __uint_as_float(u);
+  }
+  return bf16_to_f32(f32_to_bf16(f));
+}
+
+// M_t = mu * M_{t-1} + G as the momentum dtype holds it.  The product of a
+// float32 and a bf16/float32 value is exact in double, so this is the
+// correctly rounded value of the (double-evaluated) update.
+__device__ __forceinline__ float momentum_value(float mu, float mp, float g, int32_t dt) {
+  const double d = __builtin_fma(static_cast<double>(mu), static_cast<double>(mp), static_cast<double>(g));
+  return round_from_f64(d, dt);
+}
+
 // Four consecutive elements starting at idx (idx % 4 == 0 and the base
 // aligned for the dtype's 4-element vector: 16 bytes f32, 8 bytes bf16).
 __device__ __forceinline__ void load4_aligned(const void* p, int64_t idx, int32_t dt, float out[4]) {

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void k_momentum(StepArgs a, const Tile* __rest
     }
     if (in) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) mn[e] = round_to(__builtin_fmaf(a.mu, mp[e], g[e]), a.mom_dt);
+      for (int e = 0; e < 8; ++e) mn[e] = momentum_value(a.mu, mp[e], g[e], a.mom_dt);
       store8(d.mom, a.mom_dt, off, col0, n, mn);
       if (vbuf) {
         float v[8];
@@ -413,8 +413,9 @@ __global__ __launch_bounds__(256) void k_update(StepArgs a, const Tile* __restri
       } else {
         o[e] = zv[e];
       }
-      const float upd = d.update_scale * o[e] + a.weight_decay * w[e];
-      w[e] = w[e] - a.lr * upd;
+      // W - lr * (scale * O + wd * W), with the outer product-subtract fused.
+      const float upd = __builtin_fmaf(d.update_scale, o[e], a.weight_decay * w[e]);
+      w[e] = __builtin_fmaf(-a.lr, upd, w[e]);
     }
     store8(d.w, a.w_dt, off, col0, n, w);
     if (d.o_out) store8(d.o_out, DT_F32, off, col0, n, o);

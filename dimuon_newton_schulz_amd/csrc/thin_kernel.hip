@@ -1,4 +1,6 @@
-// Single-kernel step for thin matrices (Gram side k <= 32, k * N <= 32768),
+// Single-kernel step for thin matrices (Gram side k <= 32 and N within the
+// per-thread capacity: N <= 512 * CAP / KP, CAP = 32 floats for KP <= 2 and
+// 64 otherwise, KP = k rounded up to a power of two),
 // e.g. LoRA factors.  One 512-thread workgroup per matrix reads G, M_{t-1}
 // and W once and writes M_t and W once; everything else stays on chip.
 //
@@ -363,7 +365,7 @@ __global__ __launch_bounds__(TT) void k_thin(StepArgs args, const uint16_t* __re
 #pragma unroll
     for (int a = 0; a < KP; ++a)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) y[q][a][e] = round_to(__builtin_fmaf(args.mu, y[q][a][e], g[q][a][e]), args.mom_dt);
+      for (int e = 0; e < VEC; ++e) y[q][a][e] = momentum_value(args.mu, y[q][a][e], g[q][a][e], args.mom_dt);
   thin_store<KP, TALL>(d.mom, args.mom_dt, k, N, n, vec_ok, y);
   if (args.nesterov) {
 #pragma unroll
@@ -484,8 +486,8 @@ __global__ __launch_bounds__(TT) void k_thin(StepArgs args, const uint16_t* __re
         const float ov = dimuon ? post * ((dglob[a] * y[q][a][e]) * dloc[q][e]) : y[q][a][e];
         y[q][a][e] = ov;
         const float w = g[q][a][e];
-        const float upd = d.update_scale * ov + args.weight_decay * w;
-        g[q][a][e] = w - args.lr * upd;
+        const float upd = __builtin_fmaf(d.update_scale, ov, args.weight_decay * w);
+        g[q][a][e] = __builtin_fmaf(-args.lr, upd, w);
       }
   thin_store<KP, TALL>(d.w, args.w_dt, k, N, n, vec_ok, g);
   if (d.o_out) thin_store<KP, TALL>(d.o_out, DT_F32, k, N, n, vec_ok, y);

@@ -47,18 +47,20 @@
  *   - Every matrix is row-major and contiguous.  Its element size follows
  *     the dtype in the config.  Device pointers must be 16-byte aligned.
  *   - The caller owns all memory, including the workspace.  The library
- *     allocates no device memory.  It keeps one small pinned host staging
- *     buffer per (device, workspace) pair, for descriptor uploads.
+ *     allocates no device memory.  It does allocate pinned host staging
+ *     buffers (a few per host thread, and one per plan), from which the
+ *     batch's descriptor table is copied into the workspace.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
  *     default stream).  Host-side validation runs before anything is
  *     enqueued.  An invalid call returns an error code and leaves every
  *     buffer untouched.
- *   - The first bytes of the workspace cache the batch's device descriptor
- *     table.  It is re-uploaded whenever the batch (pointers, shapes,
- *     config) differs from the last call that used the same workspace.
- *     A caller who writes into the workspace between calls must call
- *     muon_workspace_invalidate() first.  Calls sharing a workspace must be
+ *   - muon_step and dimuon_step upload the descriptor table (a few KB) into
+ *     the workspace on every call.  Calls that share a workspace must be
  *     ordered, for example on one stream.
+ *   - A plan (muon_plan_create) validates and uploads once; muon_plan_step
+ *     then only launches kernels.  While a plan exists, its workspace and
+ *     every buffer it names must stay allocated, and the caller must not
+ *     write to the workspace.
  *   - Numerical edge cases are not errors.  ||M||_F = 0 gives O = 0.
  *     NaN and Inf propagate as IEEE arithmetic does.
  */
@@ -169,9 +171,22 @@ typedef enum muon_launch_kind {
  * return value is the number of events the last step recorded. */
 int32_t muon_set_launch_events(void* const* events, int32_t* kinds, int32_t n);
 
-/* Forget the cached descriptor table held in `workspace`.  The next step
- * that uses it uploads the table again. */
-void muon_workspace_invalidate(void* workspace);
+/* Prepared batch for repeated steps (an optimizer's fixed parameter list).
+ * Validation, planning and the descriptor upload happen once, in create.
+ * Each muon_plan_step runs one Muon step (dimuon = 0) or one Dimuon step
+ * (dimuon != 0) over the batch, with the same semantics as muon_step /
+ * dimuon_step.  The config, including the coefficient schedule, is copied.
+ * Errors of create: as muon_step; of step: INVALID_ARG (NULL plan), HIP. */
+typedef struct muon_plan muon_plan_t;
+muon_status_t muon_plan_create(const muon_matrix_t* mats, int64_t count,
+                               const muon_config_t* cfg, int32_t dimuon,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream, muon_plan_t** plan);
+muon_status_t muon_plan_step(muon_plan_t* plan, void* stream);
+/* Learning rate used by later steps of the plan (must be finite). */
+muon_status_t muon_plan_set_lr(muon_plan_t* plan, float lr);
+/* Waits for the plan's upload to finish, then frees the plan (NULL is a no-op). */
+void muon_plan_destroy(muon_plan_t* plan);
 
 /* Static description of a status code. */
 const char* muon_status_string(muon_status_t status);

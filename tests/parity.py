@@ -81,6 +81,16 @@ def run_oracle(wl, variant: str, cfg, index: int, scale: float = 1.0):
     return fn(to64(mt.w), to64(mt.g), to64(mt.m_prev), **kw)
 
 
+def _post_scale(ref) -> float:
+    """Dimuon's norm-fix factor s of the oracle's step O = s D_R Z D_C.
+
+    O / (d_r d_c) = s Z and ||O||_F = ||Z||_F, so s = ||O / (d_r d_c)||_F / ||O||_F."""
+    no = np.linalg.norm(ref.o)
+    if no == 0:
+        return 1.0
+    return float(np.linalg.norm(ref.o / (ref.d_r[:, None] * ref.d_c[None, :])) / no)
+
+
 def check_matrix(gpu: GpuResult, ref, i: int, cfg, variant: str, wl, scale: float = 1.0,
                  o_tol: Optional[float] = None):
     """Element-by-element comparison of matrix i; raises AssertionError with context."""
@@ -88,21 +98,31 @@ def check_matrix(gpu: GpuResult, ref, i: int, cfg, variant: str, wl, scale: floa
     o_g, o_r = gpu.o[i], ref.o
     assert np.all(np.isfinite(o_g)), f"{ctx}: non-finite O"
     if cfg.ns_dtype == "bf16":
-        err = np.max(np.abs(o_g - o_r))
+        # Max-abs at the orthogonaliser's output scale.  For Dimuon the
+        # diagonal post-scale and the norm fix are divided out (with the
+        # oracle's factors), so the bound applies to the orthogonalised
+        # matrix itself rather than to errors the factors (up to 100x) amplify.
+        scale_out = 1.0
+        if variant == "dimuon":
+            scale_out = _post_scale(ref) * ref.d_r[:, None] * ref.d_c[None, :]
+        err = np.max(np.abs(o_g - o_r) / scale_out)
         tol = TOL_BF16_MAXABS if o_tol is None else o_tol
         assert err <= tol, f"{ctx}: max|dO| = {err:.3e} > {tol}"
     else:
         err = np.linalg.norm(o_g - o_r) / max(np.linalg.norm(o_r), 1e-300)
         tol = TOL_F32_REL if o_tol is None else o_tol
         assert err <= tol, f"{ctx}: rel ||dO|| = {err:.3e} > {tol}"
-    # Momentum: within 1 ulp of its dtype.
-    dm = np.abs(gpu.m[i] - ref.m)
-    assert np.all(dm <= ulp(ref.m, cfg.mom_dtype)), f"{ctx}: momentum off by more than 1 ulp ({dm.max():.3e})"
-    # Weights: the update applied to the GPU's own O, within 1 ulp of the W dtype.
+    # Momentum: the correctly rounded value of mu * M_prev + G, bit for bit.
+    np.testing.assert_array_equal(gpu.m[i], ref.m, err_msg=f"{ctx}: momentum")
+    # Weights: the update applied to the GPU's own O.  Bound: 1 ulp of the W
+    # dtype (final rounding, plus float32 -> bf16 double rounding) plus the
+    # float32 rounding of the update term lr * (scale * O + wd * W).
     w0 = to64(wl.mats[i].w)
-    w_ref = w0 - f32(cfg.lr) * (f32(scale) * o_g + f32(cfg.weight_decay) * w0)
+    lr, wd, s = f32(cfg.lr), f32(cfg.weight_decay), f32(scale)
+    w_ref = w0 - lr * (s * o_g + wd * w0)
     dw = np.abs(gpu.w[i] - w_ref)
-    assert np.all(dw <= ulp(w_ref, cfg.w_dtype) + 1e-30), f"{ctx}: W off by more than 1 ulp ({dw.max():.3e})"
+    bound = ulp(w_ref, cfg.w_dtype) + lr * (np.abs(s * o_g) + 2 * np.abs(wd * w0)) * 2.0 ** -23
+    assert np.all(dw <= bound), f"{ctx}: W off by {(dw / bound).max():.2f} x the bound"
     # Energies: bit-exact against the oracle's float32 tree.
     if variant == "dimuon" and gpu.e[i] is not None:
         m, n = wl.mats[i].shape

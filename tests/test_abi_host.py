@@ -149,3 +149,18 @@ def test_status_strings():
     for code in range(7):
         assert D.muon_status_string(code)
     assert D.muon_status_string(99) == "unknown status"
+
+
+def test_plan_create_rejects_invalid_batches():
+    lib = D.load_library()
+    arr = _mats([(64, 256), (256, 64)])
+    c, _ = _cfg()
+    out = ctypes.c_void_p(123)
+    assert lib.muon_plan_create(arr, 2, ctypes.byref(c), 1, None, 0, None, ctypes.byref(out)) == 3
+    assert out.value is None
+    arr[1].w = arr[0].w
+    assert lib.muon_plan_create(arr, 2, ctypes.byref(c), 0, ctypes.c_void_p(0x700000000000), 1 << 40, None,
+                                ctypes.byref(out)) == 4
+    assert lib.muon_plan_step(None, None) == 1
+    assert lib.muon_plan_set_lr(None, 0.1) == 1
+    lib.muon_plan_destroy(None)
