@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="buffer sets rotated (0: automatic)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="bytes of a plain device-to-device copy run once before the workload "
+                         "(calibrates HBM byte counters against a known size)")
     return ap.parse_args()
 
 
@@ -237,6 +240,13 @@ def main():
     D.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        src = torch.ones(args.copy_probe // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     variant = args.variant or ("muon" if args.config == "c3" else "dimuon")
     wl = make_workload(args.config, dev, variant)
     work = algorithmic(wl, is_thin)
