@@ -65,32 +65,31 @@ def make_workload(name, device, variant=None):
 
 
 def algorithmic(wl, is_thin):
-    """Per-step algorithmic work: bytes of the thin path, NS flops of the MFMA path."""
+    """Per-step algorithmic work.  Thin path: bytes each pass must move (pass A
+    reads G and M_{t-1}, writes M_t; pass B reads M_t and W, writes W).  MFMA
+    path: NS flops (symmetric products counted once)."""
     size = {"f32": 4, "bf16": 2}
     per_elem = size[wl.g_dtype] + 2 * size[wl.mom_dtype] + 2 * size[wl.w_dtype]
-    thin_bytes = gram = poly = comb = 0
+    per_a = size[wl.g_dtype] + 2 * size[wl.mom_dtype]
+    per_b = size[wl.mom_dtype] + 2 * size[wl.w_dtype]
+    a_bytes = b_bytes = gram = poly = comb = 0
     for m in wl.mats:
         rows, cols = m.shape
         k, n = min(rows, cols), max(rows, cols)
         if is_thin(rows, cols):
-            thin_bytes += rows * cols * per_elem
+            a_bytes += rows * cols * per_a
+            b_bytes += rows * cols * per_b
         else:
             gram += k * k * n
             poly += k ** 3
             comb += 2 * k * k * n
-    return {"thin_bytes": thin_bytes, "gram_flops": gram, "poly_flops": poly, "comb_flops": comb,
-            "hbm_bytes_min": sum(m.shape[0] * m.shape[1] for m in wl.mats) * per_elem}
+    return {"thin_a_bytes": a_bytes, "thin_b_bytes": b_bytes, "gram_flops": gram, "poly_flops": poly,
+            "comb_flops": comb, "hbm_bytes_min": sum(m.shape[0] * m.shape[1] for m in wl.mats) * per_elem}
 
 
 def is_thin(m, n):
-    """Same rule as the library's planner: Gram side <= 32 and the long side
-    within the single-workgroup kernel's capacity."""
-    k, big = min(m, n), max(m, n)
-    p = 1
-    while p < k:
-        p *= 2
-    cap = 32 if p <= 2 else 64
-    return k <= 32 and big <= 512 * cap // p
+    """Same rule as the library's planner: Gram side <= 32."""
+    return min(m, n) <= 32
 
 
 def measure(wl, steps, warmup, sets, ns_dtype=None):
@@ -162,12 +161,13 @@ def roofline_for(wl, cfg, per_kind, work, steps):
     tot_ms, launches = per_kind[kind]
     avg_ms = tot_ms / launches
     per_launch_iters = 1
-    if kind == "thin":
-        achieved = work["thin_bytes"] / (avg_ms * 1e-3) / 1e9
+    if kind in ("thin_a", "thin_b"):
+        nbytes = work[kind + "_bytes"]
+        achieved = nbytes / (avg_ms * 1e-3) / 1e9
         return kind, {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                       "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                      "kernel": "k_thin", "avg_launch_ms": round(avg_ms, 5),
-                      "bytes_per_launch": work["thin_bytes"]}
+                      "kernel": "k_" + kind, "avg_launch_ms": round(avg_ms, 5),
+                      "bytes_per_launch": nbytes}
     flops = {"combine": work["comb_flops"], "gram": work["gram_flops"], "poly": work["poly_flops"]}.get(kind)
     if flops is None:
         # a streaming kernel dominates: report bytes of one pass

@@ -31,10 +31,11 @@ STATUS_NAMES = {0: "MUON_OK", 1: "MUON_ERR_INVALID_ARG", 2: "MUON_ERR_DTYPE",
 
 EXPORTED_SYMBOLS = ("muon_config_default", "muon_workspace_bytes", "muon_step", "dimuon_step",
                     "muon_set_launch_events", "muon_plan_create", "muon_plan_step", "muon_plan_set_lr",
-                    "muon_plan_destroy", "muon_status_string", "muon_last_error", "muon_abi_version")
+                    "muon_plan_reset", "muon_plan_destroy", "muon_status_string", "muon_last_error", "muon_abi_version")
 
-LAUNCH_KINDS = {-1: "start", 0: "thin", 1: "momentum", 2: "condition", 3: "prescale", 4: "norm",
-                5: "gram", 6: "poly", 7: "combine", 8: "postnorm", 9: "update"}
+LAUNCH_KINDS = {-1: "start", 0: "thin_b", 1: "momentum", 2: "condition", 3: "prescale", 4: "norm",
+                5: "gram", 6: "poly", 7: "combine", 8: "postnorm", 9: "update", 10: "thin_energy",
+                11: "thin_a"}
 
 
 class MuonMatrix(ctypes.Structure):
@@ -92,6 +93,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.muon_plan_step.restype = ctypes.c_int
     lib.muon_plan_set_lr.argtypes = [ctypes.c_void_p, ctypes.c_float]
     lib.muon_plan_set_lr.restype = ctypes.c_int
+    lib.muon_plan_reset.argtypes = [ctypes.c_void_p]
+    lib.muon_plan_reset.restype = ctypes.c_int
     lib.muon_plan_destroy.argtypes = [ctypes.c_void_p]
     lib.muon_plan_destroy.restype = None
     lib.muon_status_string.argtypes = [ctypes.c_int]
@@ -319,6 +322,10 @@ class Plan:
 
     def set_lr(self, lr: float):
         _check(self._lib.muon_plan_set_lr(self._handle, lr))
+
+    def reset(self):
+        """Call after writing to the momentum buffers outside the plan."""
+        _check(self._lib.muon_plan_reset(self._handle))
 
     def close(self):
         if self._handle:

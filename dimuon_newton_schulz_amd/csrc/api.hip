@@ -69,8 +69,9 @@ struct Plan {
   std::vector<MatDesc> desc;
   std::vector<Tile> k1, k3, syrk, comb, k5;
   std::vector<uint16_t> gen;
-  // thin matrices grouped by (KP, tall)
-  struct ThinGroup { int kp; bool tall; std::vector<uint16_t> ids; size_t off; };
+  // thin matrices grouped by padded Gram side KP; one tile (matrix, slice)
+  // per workgroup, one launch per phase and KP
+  struct ThinGroup { int kp; std::vector<Tile> tiles; size_t off; };
   std::vector<ThinGroup> thin;
   // byte offsets in the workspace
   size_t desc_off = 0, scal_off = 0, k1_off = 0, k3_off = 0, syrk_off = 0, comb_off = 0, k5_off = 0, gen_off = 0;
@@ -79,15 +80,10 @@ struct Plan {
   std::vector<unsigned char> table;
 };
 
-// The thin kernel holds CAP floats of the matrix per thread (512 threads):
-// CAP = 32 for a padded Gram side KP <= 2, else 64, so N <= 512 * CAP / KP.
-bool is_thin(int64_t m, int64_t n) {
-  const int64_t k = std::min(m, n), N = std::max(m, n);
-  if (k > kThinMaxK) return false;
-  const int64_t kp = next_pow2(k);
-  const int64_t cap = kp <= 2 ? 32 : 64;
-  return N <= 512 * cap / kp;
-}
+// Thin path: Gram side k <= 32.  Each slice of the long side is one
+// 256-thread workgroup holding 32 values per thread, i.e. 8192 / KP positions.
+bool is_thin(int64_t m, int64_t n) { return std::min(m, n) <= kThinMaxK; }
+inline int thin_slice_len(int kp) { return 256 * (32 / kp); }
 
 muon_status_t validate_config(const muon_config_t* cfg) {
   if (!cfg) return fail(MUON_ERR_INVALID_ARG, "cfg is NULL");
@@ -180,7 +176,7 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
                          Plan& p) {
   const size_t es = dtype_size(cfg->ns_dtype);
   p.desc.assign(count, MatDesc{});
-  std::map<std::pair<int, bool>, std::vector<uint16_t>> thin_groups;
+  std::map<int, std::vector<Tile>> thin_groups;
   for (int64_t i = 0; i < count; ++i) {
     const muon_matrix_t& x = mats[i];
     MatDesc& d = p.desc[i];
@@ -200,7 +196,10 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
     if (is_thin(x.m, x.n)) {
       d.KP = next_pow2(d.k);
       d.NP = d.N;
-      thin_groups[{d.KP, d.tall != 0}].push_back(static_cast<uint16_t>(i));
+      d.L = thin_slice_len(d.KP);
+      d.S = static_cast<int32_t>(ceil_div(d.N, d.L));
+      for (int sl = 0; sl < d.S; ++sl)
+        thin_groups[d.KP].push_back({static_cast<uint16_t>(i), static_cast<uint16_t>(sl), 0, 0});
     } else {
       d.KP = static_cast<int32_t>(round_up(d.k, kPad));
       d.NP = static_cast<int32_t>(round_up(d.N, kPad));
@@ -221,7 +220,8 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
         for (int tj = 0; tj < ceil_div(d.n, 64); ++tj) p.k5.push_back({static_cast<uint16_t>(i), (uint16_t)ti, (uint16_t)tj, 0});
     }
   }
-  for (auto& kv : thin_groups) p.thin.push_back({kv.first.first, kv.first.second, kv.second, 0});
+  for (auto& kv : thin_groups) p.thin.push_back({kv.first, kv.second, 0});
+  if (count > 65535) return fail(MUON_ERR_UNSUPPORTED, "too many matrices");
 
   // Table prefix: descriptors, scalars, tile lists, id lists.
   size_t off = kAlign;   // first 256 bytes reserved
@@ -238,9 +238,22 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
   p.comb_off = take(sizeof(Tile) * p.comb.size());
   p.k5_off = take(sizeof(Tile) * p.k5.size());
   p.gen_off = take(sizeof(uint16_t) * p.gen.size());
-  for (auto& g : p.thin) g.off = take(sizeof(uint16_t) * g.ids.size());
+  for (auto& g : p.thin) g.off = take(sizeof(Tile) * g.tiles.size());
   p.table_bytes = off;
 
+  // Per-matrix scratch of the thin path.
+  for (int64_t i = 0; i < count; ++i) {
+    MatDesc& d = p.desc[i];
+    if (d.S == 0) continue;
+    const size_t npair = static_cast<size_t>(d.KP) * (d.KP + 1) / 2;
+    const size_t cache = (static_cast<size_t>(d.S) * d.KP + d.N + d.S) * 4;
+    d.te_off[0] = take(cache);
+    d.te_off[1] = take(cache);
+    d.tdl_off = take(static_cast<size_t>(d.N) * 4);
+    d.tdg_off = take(static_cast<size_t>(d.KP) * 4);
+    d.tg_off = take(static_cast<size_t>(d.S) * npair * 8);
+    d.tg2_off = take(static_cast<size_t>(d.S) * npair * 8);
+  }
   // Per-matrix scratch of the general path.
   for (uint16_t i : p.gen) {
     MatDesc& d = p.desc[i];
@@ -268,7 +281,7 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
     put(p.table, p.comb_off, p.comb);
     put(p.table, p.k5_off, p.k5);
     put(p.table, p.gen_off, p.gen);
-    for (auto& g : p.thin) put(p.table, g.off, g.ids);
+    for (auto& g : p.thin) put(p.table, g.off, g.tiles);
   }
   return MUON_OK;
 }
@@ -410,16 +423,22 @@ void make_coeffs(const muon_config_t& cfg, Coeffs* cf) {
 
 // The launch sequence of one step; the descriptor table is already on the
 // device (ordered before these launches on stream s).
+// `parity` selects the thin path's energy cache holding the energies of
+// M_{t-1}; `cached` says whether it is valid (else it is computed first).
 muon_status_t launch_all(const Plan& p, const StepArgs& a, const Coeffs* cf, int ns_steps, bool dimuon,
-                         hipStream_t s) {
+                         int parity, bool cached, hipStream_t s) {
   char* base = a.ws;
   auto tl = [&](size_t off) { return reinterpret_cast<const Tile*>(base + off); };
   auto il = [&](size_t off) { return reinterpret_cast<const uint16_t*>(base + off); };
   g_hook.next = 0;
   MUON_HIP_TRY(hook_record(MUON_LAUNCH_START, s));
-  for (const auto& g : p.thin)
-    MUON_LAUNCH(MUON_LAUNCH_THIN,
-                launch_thin(a, il(g.off), static_cast<int>(g.ids.size()), g.kp, g.tall, ns_steps, cf, s));
+  for (const auto& g : p.thin) {
+    const int nt = static_cast<int>(g.tiles.size());
+    if (dimuon && !cached)
+      MUON_LAUNCH(MUON_LAUNCH_THIN_ENERGY, launch_thin_energy(a, tl(g.off), nt, g.kp, parity, s));
+    MUON_LAUNCH(MUON_LAUNCH_THIN_A, launch_thin_a(a, tl(g.off), nt, g.kp, parity, s));
+    MUON_LAUNCH(MUON_LAUNCH_THIN, launch_thin_b(a, tl(g.off), nt, g.kp, ns_steps, cf, s));
+  }
   if (!p.gen.empty()) {
     const int ng = static_cast<int>(p.gen.size());
     MUON_LAUNCH(MUON_LAUNCH_MOMENTUM, launch_momentum(a, tl(p.k1_off), static_cast<int>(p.k1.size()), dimuon, s));
@@ -457,7 +476,7 @@ muon_status_t run_step(const muon_matrix_t* mats, int64_t count, const muon_conf
   if ((st = slot.upload(p.table, ws, s)) != MUON_OK) return st;
   Coeffs cf[kMaxSteps];
   make_coeffs(*cfg, cf);
-  return launch_all(p, make_args(p, *cfg, ws, dimuon), cf, cfg->ns_steps, dimuon, s);
+  return launch_all(p, make_args(p, *cfg, ws, dimuon), cf, cfg->ns_steps, dimuon, 0, false, s);
 }
 
 }  // namespace
@@ -472,6 +491,8 @@ struct muon_plan {
   bool dimuon;
   void* ws;
   muon::Staging staging;
+  int parity = 0;          // energy cache holding the energies of the current momentum
+  bool cached = false;     // whether that cache is valid
 };
 
 // ---------------------------------------------------------------------------
@@ -561,8 +582,22 @@ muon_status_t muon_plan_step(muon_plan_t* plan, void* stream) {
   using namespace muon;
   g_last_error.clear();
   if (!plan) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
-  return launch_all(plan->p, make_args(plan->p, plan->cfg, plan->ws, plan->dimuon), plan->cf, plan->cfg.ns_steps,
-                    plan->dimuon, static_cast<hipStream_t>(stream));
+  const muon_status_t st = launch_all(plan->p, make_args(plan->p, plan->cfg, plan->ws, plan->dimuon), plan->cf,
+                                      plan->cfg.ns_steps, plan->dimuon, plan->parity, plan->cached,
+                                      static_cast<hipStream_t>(stream));
+  if (st == MUON_OK && plan->dimuon) {
+    // Pass A wrote the energies of the new momentum into the other cache.
+    plan->parity ^= 1;
+    plan->cached = true;
+  }
+  return st;
+}
+
+muon_status_t muon_plan_reset(muon_plan_t* plan) {
+  using namespace muon;
+  if (!plan) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
+  plan->cached = false;
+  return MUON_OK;
 }
 
 muon_status_t muon_plan_set_lr(muon_plan_t* plan, float lr) {

@@ -44,7 +44,14 @@ struct alignas(16) MatDesc {
   int32_t ncb, nrb;       // number of 512-column / 32-row energy blocks
   int32_t n_pn, n_pz;     // partial counts
   int32_t scal_idx;       // index into the per-matrix scalar array
-  int32_t pad0;
+  // Thin path (Gram side <= 32): the long side is cut into S slices of L positions.
+  int32_t S, L;
+  int64_t te_off[2];      // energy cache, two parities: [S][KP] row partials, [N] per-position
+                          // energies, [S] slice maxima (f32)
+  int64_t tdl_off;        // per-position factors d_loc [N] f32
+  int64_t tdg_off;        // Gram-side factors d_glob [KP] f32
+  int64_t tg_off;         // Gram partials [S][KP(KP+1)/2] f64
+  int64_t tg2_off;        // d_loc^2-weighted Gram partials [S][KP(KP+1)/2] f64
 };
 
 // Per-matrix scalars written on the device during a step.
@@ -159,25 +166,60 @@ __device__ __forceinline__ void store4_aligned(void* p, int64_t idx, int32_t dt,
   }
 }
 
-// Wave64 butterfly sum: after it every lane holds the pairwise-tree sum of
-// the 64 lane values (lane groups of 2, 4, ... 64 combined left + right;
-// IEEE addition is commutative, so lane L and lane L^off agree).
+// Cross-lane moves within a wave64 (DPP: no LDS traffic).  quad_perm
+// [1,0,3,2] and [2,3,0,1] pair lanes L and L^1, L^2; row_half_mirror maps
+// lane i of each 8-lane group to 7-i; row_mirror maps lane i of each
+// 16-lane row to 15-i.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(b), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), lane);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), lane);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+
+// Wave64 pairwise-tree sum; every lane receives the result.  Level 1 adds
+// lanes (2j, 2j+1), level 2 the pairs of pairs, level 3 the 4-lane blocks,
+// level 4 the 8-lane blocks, then the four 16-lane row sums r0..r3 are added
+// as (r0 + r1) + (r2 + r3).  After each level every lane of a block holds the
+// block's sum, so pairing with any lane of the partner block gives the same
+// value, and IEEE addition is commutative: this is exactly the pairwise tree
+// over the 64 lane values in lane order.
 __device__ __forceinline__ float wave_tree_sum(float v) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) v = v + __shfl_xor(v, off, 64);
-  return v;
+  v = v + dpp_f32<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = v + dpp_f32<0x4E>(v);    // quad_perm [2,3,0,1]
+  v = v + dpp_f32<0x141>(v);   // row_half_mirror
+  v = v + dpp_f32<0x140>(v);   // row_mirror
+  return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) v = v + __shfl_xor(v, off, 64);
-  return v;
+  v = v + dpp_f64<0xB1>(v);
+  v = v + dpp_f64<0x4E>(v);
+  v = v + dpp_f64<0x141>(v);
+  v = v + dpp_f64<0x140>(v);
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
+  return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)), fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
 }
 
 // Pairwise-tree sum of p[0], p[stride], ..., p[(count-1)*stride], zero-padded
@@ -235,7 +277,13 @@ hipError_t launch_syrk(const StepArgs& a, const Tile* tiles, int n, int kind, in
 // buffers; `product` false skips B X (used when ns_steps is 0).
 hipError_t launch_combine(const StepArgs& a, const Tile* tiles, int n, int src_x, int dst_x,
                           bool first, bool last, bool product, Coeffs cf, hipStream_t s);
-hipError_t launch_thin(const StepArgs& a, const uint16_t* mats, int n, int kp, bool tall,
-                       int ns_steps, const Coeffs* cf, hipStream_t s);
+// Thin path, one launch per phase over all slices of one padded Gram side KP:
+// energies of M_{t-1} (only when no cached energies exist), pass A
+// (momentum, next energies, Gram partials), pass B (k x k iteration, apply,
+// update).  `parity` selects the energy cache read; pass A writes the other.
+hipError_t launch_thin_energy(const StepArgs& a, const Tile* tiles, int n, int kp, int parity, hipStream_t s);
+hipError_t launch_thin_a(const StepArgs& a, const Tile* tiles, int n, int kp, int parity, hipStream_t s);
+hipError_t launch_thin_b(const StepArgs& a, const Tile* tiles, int n, int kp, int ns_steps, const Coeffs* cf,
+                         hipStream_t s);
 
 }  // namespace muon

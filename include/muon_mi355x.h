@@ -150,7 +150,7 @@ muon_status_t dimuon_step(const muon_matrix_t* mats, int64_t count,
 /* Kernel kinds reported by the launch-event hook. */
 typedef enum muon_launch_kind {
   MUON_LAUNCH_START = -1,     /* event recorded before the first launch */
-  MUON_LAUNCH_THIN = 0,       /* fused single-kernel step, Gram side <= 32 */
+  MUON_LAUNCH_THIN = 0,       /* thin path pass B: k x k iteration, apply, update */
   MUON_LAUNCH_MOMENTUM = 1,   /* momentum (+ energy partials) */
   MUON_LAUNCH_CONDITION = 2,  /* energies -> Dimuon factors */
   MUON_LAUNCH_PRESCALE = 3,   /* conditioned, normalised bf16/f32 copy (+ transpose) */
@@ -159,7 +159,9 @@ typedef enum muon_launch_kind {
   MUON_LAUNCH_POLY = 6,       /* B = b A + c A A */
   MUON_LAUNCH_COMBINE = 7,    /* X = a X + B X */
   MUON_LAUNCH_POSTNORM = 8,   /* Dimuon norm fix */
-  MUON_LAUNCH_UPDATE = 9      /* O and the weight update */
+  MUON_LAUNCH_UPDATE = 9,     /* O and the weight update */
+  MUON_LAUNCH_THIN_ENERGY = 10, /* thin path: energies of M_{t-1} (no cached energies) */
+  MUON_LAUNCH_THIN_A = 11     /* thin path pass A: momentum, next energies, Gram partials */
 } muon_launch_kind_t;
 
 /* Timing hook, per host thread; not part of the method.  When `events` is
@@ -183,6 +185,12 @@ muon_status_t muon_plan_create(const muon_matrix_t* mats, int64_t count,
                                void* workspace, size_t workspace_bytes,
                                void* stream, muon_plan_t** plan);
 muon_status_t muon_plan_step(muon_plan_t* plan, void* stream);
+/* A Dimuon plan keeps, in its workspace, the row/column energies of the
+ * momentum its last step wrote (the next step's R and C), so for matrices
+ * with a Gram side <= 32 the next step need not read M_{t-1} twice.  Call
+ * muon_plan_reset after writing to the momentum buffers outside the plan
+ * (resume, reset); the next step then recomputes them.  Muon plans ignore it. */
+muon_status_t muon_plan_reset(muon_plan_t* plan);
 /* Learning rate used by later steps of the plan (must be finite). */
 muon_status_t muon_plan_set_lr(muon_plan_t* plan, float lr);
 /* Waits for the plan's upload to finish, then frees the plan (NULL is a no-op). */

@@ -205,3 +205,30 @@ def test_plan_matches_stateless_step_bitwise():
                           mom_dtype="bf16", w_dtype="bf16", eps=f32(cfg.dimuon_eps))
         assert np.max(np.abs(to64(p.o_out) - r.o)) < 2e-2
     plan.close()
+
+
+@pytest.mark.parametrize("shapes", [[(8, 4096), (4096, 8), (3, 1000), (16, 2048)], [(300, 700), (8, 300)]])
+def test_plan_steps_with_cached_energies_match_stateless(shapes):
+    # A Dimuon plan reuses the energies its previous step computed; three plan
+    # steps must equal three stateless steps bit for bit, and a reset must be
+    # harmless.
+    wl = W.random_batch(shapes, dtype="f32", ns_dtype="bf16", seed=14, variant="dimuon")
+    cfg = cfg_of(wl)
+    announce(f"cached energies {shapes}")
+    def fresh():
+        return [D.Param(w=m.w.cuda().clone(), g=m.g.cuda().clone(), mom=m.m_prev.cuda().clone(),
+                        o_out=torch.empty(m.shape, device="cuda"),
+                        energy_out=torch.empty(m.shape[0] + m.shape[1], device="cuda")) for m in wl.mats]
+    a, b = fresh(), fresh()
+    plan = D.Plan(a, cfg, dimuon=True)
+    for step in range(3):
+        if step == 2:
+            plan.reset()
+        plan.step()
+        D.dimuon_step(b, cfg)
+        torch.cuda.synchronize()
+        for pa, pb in zip(a, b):
+            for name in ("w", "mom", "o_out", "energy_out"):
+                np.testing.assert_array_equal(getattr(pa, name).cpu().numpy(), getattr(pb, name).cpu().numpy(),
+                                              err_msg=f"step {step} {name}")
+    plan.close()
