@@ -83,7 +83,6 @@ struct Plan {
 // Thin path: Gram side k <= 32.  Each slice of the long side is one
 // 256-thread workgroup holding 32 values per thread, i.e. 8192 / KP positions.
 bool is_thin(int64_t m, int64_t n) { return std::min(m, n) <= kThinMaxK; }
-inline int thin_slice_len(int kp) { return 256 * (32 / kp); }
 
 muon_status_t validate_config(const muon_config_t* cfg) {
   if (!cfg) return fail(MUON_ERR_INVALID_ARG, "cfg is NULL");
@@ -437,7 +436,7 @@ muon_status_t launch_all(const Plan& p, const StepArgs& a, const Coeffs* cf, int
     if (dimuon && !cached)
       MUON_LAUNCH(MUON_LAUNCH_THIN_ENERGY, launch_thin_energy(a, tl(g.off), nt, g.kp, parity, s));
     MUON_LAUNCH(MUON_LAUNCH_THIN_A, launch_thin_a(a, tl(g.off), nt, g.kp, parity, s));
-    MUON_LAUNCH(MUON_LAUNCH_THIN, launch_thin_b(a, tl(g.off), nt, g.kp, ns_steps, cf, s));
+    MUON_LAUNCH(MUON_LAUNCH_THIN, launch_thin_b(a, tl(g.off), nt, g.kp, ns_steps, cf, parity, s));
   }
   if (!p.gen.empty()) {
     const int ng = static_cast<int>(p.gen.size());

@@ -16,6 +16,14 @@ namespace muon {
 constexpr int kPad = 128;          // padding granularity of workspace matrices
 constexpr int kMaxSteps = 32;      // largest ns_steps accepted
 
+// Thin path geometry, shared by the planner and the kernels: one 256-thread
+// workgroup per slice of the long side; a thread owns VEC consecutive
+// positions of all KP Gram-side rows (KP = k rounded up to a power of two),
+// max(16, KP) values per array.
+constexpr int kThinThreads = 256;
+__host__ __device__ constexpr int thin_vec(int kp) { return (kp < 16 ? 16 : kp) / kp; }
+__host__ __device__ constexpr int thin_slice_len(int kp) { return kThinThreads * thin_vec(kp); }
+
 enum DType : int32_t { DT_F32 = 0, DT_BF16 = 1 };
 
 // Per-matrix device descriptor (uploaded once per batch into the workspace).
@@ -88,6 +96,19 @@ struct StepArgs {
 // --------------------------------------------------------------------------
 #if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
 
+// Global-memory pointers.  Pointers read from the descriptor table are
+// generic, which makes the compiler emit flat accesses; flat accesses also
+// count against the LDS counter, so an LDS-only barrier would wait for them.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define MUON_GLOBAL __attribute__((address_space(1)))
+#else
+#define MUON_GLOBAL
+#endif
+template <typename T>
+__device__ __forceinline__ MUON_GLOBAL T* gmem(T* p) { return (MUON_GLOBAL T*)(p); }
+template <typename T>
+__device__ __forceinline__ const MUON_GLOBAL T* gmem(const T* p) { return (const MUON_GLOBAL T*)(p); }
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
@@ -101,13 +122,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 __device__ __forceinline__ float load_elem(const void* p, int64_t idx, int32_t dt) {
-  if (dt == DT_F32) return static_cast<const float*>(p)[idx];
-  return bf16_to_f32(static_cast<const uint16_t*>(p)[idx]);
+  if (dt == DT_F32) return gmem(static_cast<const float*>(p))[idx];
+  return bf16_to_f32(gmem(static_cast<const uint16_t*>(p))[idx]);
 }
 
 __device__ __forceinline__ void store_elem(void* p, int64_t idx, int32_t dt, float v) {
-  if (dt == DT_F32) static_cast<float*>(p)[idx] = v;
-  else static_cast<uint16_t*>(p)[idx] = f32_to_bf16(v);
+  if (dt == DT_F32) gmem(static_cast<float*>(p))[idx] = v;
+  else gmem(static_cast<uint16_t*>(p))[idx] = f32_to_bf16(v);
 }
 
 // Value a tensor of dtype dt holds after storing v.
@@ -144,10 +165,10 @@ __device__ __forceinline__ float momentum_value(float mu, float mp, float g, int
 // aligned for the dtype's 4-element vector: 16 bytes f32, 8 bytes bf16).
 __device__ __forceinline__ void load4_aligned(const void* p, int64_t idx, int32_t dt, float out[4]) {
   if (dt == DT_F32) {
-    float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + idx);
+    float4 v = *reinterpret_cast<const MUON_GLOBAL float4*>(gmem(static_cast<const float*>(p)) + idx);
     out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
   } else {
-    uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + idx);
+    uint2 v = *reinterpret_cast<const MUON_GLOBAL uint2*>(gmem(static_cast<const uint16_t*>(p)) + idx);
     out[0] = __uint_as_float(v.x << 16);
     out[1] = __uint_as_float(v.x & 0xffff0000u);
     out[2] = __uint_as_float(v.y << 16);
@@ -157,12 +178,12 @@ __device__ __forceinline__ void load4_aligned(const void* p, int64_t idx, int32_
 
 __device__ __forceinline__ void store4_aligned(void* p, int64_t idx, int32_t dt, const float v[4]) {
   if (dt == DT_F32) {
-    *reinterpret_cast<float4*>(static_cast<float*>(p) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<MUON_GLOBAL float4*>(gmem(static_cast<float*>(p)) + idx) = make_float4(v[0], v[1], v[2], v[3]);
   } else {
     uint2 u;
     u.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
     u.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + idx) = u;
+    *reinterpret_cast<MUON_GLOBAL uint2*>(gmem(static_cast<uint16_t*>(p)) + idx) = u;
   }
 }
 
@@ -242,6 +263,47 @@ __device__ __forceinline__ float pairwise_strided(const float* p, int count, int
   return stack[top];
 }
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// waits for every outstanding global load and store of the wave; kernels
+// whose global writes are never read back by the same launch use this one so
+// that loads and stores stay in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Pairwise-tree sum of count values p[0], p[stride], ... zero-padded to a
+// power of two, with the loads issued eight at a time (aligned blocks of
+// eight are complete subtrees of the padded tree; a padding block adds +0 to
+// non-negative sums, so padding to a multiple of eight gives the same value).
+// first8 holds the first block, loaded by the caller (zeros beyond count).
+__device__ __forceinline__ float pairwise_strided8(const float (&first8)[8], const float* p, int count,
+                                                   int64_t stride) {
+  float stack[24];
+  const int blocks = (count + 7) / 8;
+  int pow2 = 1;
+  while (pow2 < blocks) pow2 <<= 1;
+  for (int t = 0; t < pow2; ++t) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = t * 8 + j;
+      v[j] = (t == 0) ? first8[j] : ((i < count) ? gmem(p)[static_cast<int64_t>(i) * stride] : 0.0f);
+    }
+    float carry = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    int j = 0;
+    while ((t >> j) & 1) {
+      carry = stack[j] + carry;
+      ++j;
+    }
+    stack[j] = carry;
+  }
+  int top = 0;
+  while ((1 << top) < pow2) ++top;
+  return stack[top];
+}
+
 // Conditioning factor (relative energy + eps)^(-1/4).
 __device__ __forceinline__ float cond_factor(float e, float emax, float eps) {
   float rho = e / emax;
@@ -279,11 +341,12 @@ hipError_t launch_combine(const StepArgs& a, const Tile* tiles, int n, int src_x
                           bool first, bool last, bool product, Coeffs cf, hipStream_t s);
 // Thin path, one launch per phase over all slices of one padded Gram side KP:
 // energies of M_{t-1} (only when no cached energies exist), pass A
-// (momentum, next energies, Gram partials), pass B (k x k iteration, apply,
-// update).  `parity` selects the energy cache read; pass A writes the other.
+// (momentum, Gram partials), pass B (k x k iteration, energies of M_t, apply,
+// update).  `parity` selects the energy cache pass A reads; pass B writes the
+// other.
 hipError_t launch_thin_energy(const StepArgs& a, const Tile* tiles, int n, int kp, int parity, hipStream_t s);
 hipError_t launch_thin_a(const StepArgs& a, const Tile* tiles, int n, int kp, int parity, hipStream_t s);
 hipError_t launch_thin_b(const StepArgs& a, const Tile* tiles, int n, int kp, int ns_steps, const Coeffs* cf,
-                         hipStream_t s);
+                         int parity, hipStream_t s);
 
 }  // namespace muon

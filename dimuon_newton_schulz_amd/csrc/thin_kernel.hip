@@ -16,12 +16,12 @@
 // a different order.
 //
 // A step is two launches:
-//   pass A  momentum (stored), energies of the new momentum for the next step,
-//           conditioned input Y, per-slice Gram partials (plain and d_loc^2
-//           weighted) through LDS.
+//   pass A  momentum (stored), conditioned input Y, per-slice Gram partials
+//           (plain and d_loc^2 weighted).
 //   pass B  reduce the partials, k x k iteration (one wave for KP <= 8) while
-//           M_t and W are loading, apply Z, Dimuon post-scale with the norm
-//           fix computed in Gram space, weight update.
+//           M_t and W are loading, energies of M_t for the next step, apply Z,
+//           Dimuon post-scale with the norm fix computed in Gram space,
+//           weight update.
 // Dimuon's factors come from the energies of M_{t-1}.  The step that wrote
 // M_{t-1} left them in the workspace energy cache ("Dimuon: LoRA 에 맞춰 다시
 // 짠 Muon", section "왜 「지난」 모멘텀인가", notes that R and C can be computed
@@ -40,13 +40,13 @@
 
 namespace muon {
 
-constexpr int TT = 256;          // threads per workgroup (one slice)
-constexpr int NWV = TT / 64;     // waves per workgroup
+constexpr int TT = kThinThreads;   // threads per workgroup (one slice)
+constexpr int NWV = TT / 64;       // waves per workgroup
 
 template <int KP>
 struct TS {
-  static constexpr int VEC = 32 / KP;          // positions per thread
-  static constexpr int L = TT * VEC;            // positions per slice
+  static constexpr int VEC = thin_vec(KP);      // positions per thread
+  static constexpr int L = thin_slice_len(KP);  // positions per slice
   static constexpr int NPAIR = KP * (KP + 1) / 2;
   static constexpr int C = VEC < 4 ? VEC : 4;   // wide: elements per vector access
   static constexpr int CT = KP < 4 ? KP : 4;    // tall: elements per vector access
@@ -56,121 +56,153 @@ struct ThinCoeffs {
   Coeffs c[kMaxSteps];
 };
 
-template <int CNT>
-__device__ __forceinline__ void load_run(const void* p, int32_t dt, int64_t idx, int avail, bool vec_ok,
-                                         float* out) {
-  if (vec_ok && avail >= CNT) {
-    if constexpr (CNT == 4) {
-      load4_aligned(p, idx, dt, out);
-      return;
-    } else if constexpr (CNT == 2) {
-      if (dt == DT_F32) {
-        const float2 v = *reinterpret_cast<const float2*>(static_cast<const float*>(p) + idx);
-        out[0] = v.x; out[1] = v.y;
-      } else {
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p) + idx);
-        out[0] = __uint_as_float(v << 16); out[1] = __uint_as_float(v & 0xffff0000u);
-      }
-      return;
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < CNT; ++e) out[e] = (e < avail) ? load_elem(p, idx + e, dt) : 0.0f;
+// Storage element types: float (f32) and uint16_t (bf16 bits).
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(uint16_t x) { return bf16_to_f32(x); }
+template <typename S>
+__device__ __forceinline__ S from_f(float v) {
+  if constexpr (sizeof(S) == 4) return v;
+  else return f32_to_bf16(v);
 }
 
-template <int CNT>
-__device__ __forceinline__ void store_run(void* p, int32_t dt, int64_t idx, int avail, bool vec_ok,
-                                          const float* v) {
-  if (vec_ok && avail >= CNT) {
-    if constexpr (CNT == 4) {
-      store4_aligned(p, idx, dt, v);
-      return;
-    } else if constexpr (CNT == 2) {
-      if (dt == DT_F32) {
-        *reinterpret_cast<float2*>(static_cast<float*>(p) + idx) = make_float2(v[0], v[1]);
-      } else {
-        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p) + idx) =
-            f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-      }
-      return;
+// C consecutive elements as one aligned access (p aligned to C elements).
+template <typename S, int C>
+__device__ __forceinline__ void vload(const MUON_GLOBAL S* p, float* out) {
+  if constexpr (C == 1) {
+    out[0] = to_f(p[0]);
+  } else if constexpr (sizeof(S) == 4) {
+    if constexpr (C == 4) {
+      const float4 v = *reinterpret_cast<const MUON_GLOBAL float4*>(p);
+      out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+    } else {
+      const float2 v = *reinterpret_cast<const MUON_GLOBAL float2*>(p);
+      out[0] = v.x; out[1] = v.y;
+    }
+  } else {
+    if constexpr (C == 4) {
+      const uint2 v = *reinterpret_cast<const MUON_GLOBAL uint2*>(p);
+      out[0] = __uint_as_float(v.x << 16); out[1] = __uint_as_float(v.x & 0xffff0000u);
+      out[2] = __uint_as_float(v.y << 16); out[3] = __uint_as_float(v.y & 0xffff0000u);
+    } else {
+      const uint32_t v = *reinterpret_cast<const MUON_GLOBAL uint32_t*>(p);
+      out[0] = __uint_as_float(v << 16); out[1] = __uint_as_float(v & 0xffff0000u);
     }
   }
-#pragma unroll
-  for (int e = 0; e < CNT; ++e)
-    if (e < avail) store_elem(p, idx + e, dt, v[e]);
 }
 
-__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+template <typename S, int C>
+__device__ __forceinline__ void vstore(MUON_GLOBAL S* p, const float* v) {
+  if constexpr (C == 1) {
+    p[0] = from_f<S>(v[0]);
+  } else if constexpr (sizeof(S) == 4) {
+    if constexpr (C == 4) *reinterpret_cast<MUON_GLOBAL float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    else *reinterpret_cast<MUON_GLOBAL float2*>(p) = make_float2(v[0], v[1]);
+  } else {
+    if constexpr (C == 4) {
+      uint2 u;
+      u.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+      u.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+      *reinterpret_cast<MUON_GLOBAL uint2*>(p) = u;
+    } else {
+      *reinterpret_cast<MUON_GLOBAL uint32_t*>(p) =
+          static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+    }
+  }
+}
+
+// Index of element (a, l) of the Gram orientation in the caller's row-major m x n array.
+template <bool TALL>
+__device__ __forceinline__ int64_t gidx(int a, int l, int n) {
+  return TALL ? static_cast<int64_t>(l) * n + a : static_cast<int64_t>(a) * n + l;
+}
+
+// Elements per vector access of a slice: along the positions (wide) or along
+// the Gram-side rows (tall, where a row of the caller's array holds k values).
+template <int KP, bool TALL>
+constexpr int slice_vec() { return TALL ? TS<KP>::CT : TS<KP>::C; }
+
+// A slice is "full" when all KP rows exist, all its positions are inside N
+// and every vector access is aligned; then no access needs a predicate.
+template <int KP, bool TALL>
+__device__ __forceinline__ bool slice_full(int k, int N, int n, int s) {
+  return k == KP && (s + 1) * TS<KP>::L <= N && (n % slice_vec<KP, TALL>()) == 0;
+}
 
 // v[a][e] = element (a, l0 + e) of the Gram orientation; 0 outside k x N.
-template <int KP, bool TALL>
-__device__ __forceinline__ void slice_load(const void* p, int32_t dt, int k, int N, int n, int l0,
-                                           float (&v)[KP][TS<KP>::VEC]) {
-  constexpr int VEC = TS<KP>::VEC;
-  if constexpr (!TALL) {
-    constexpr int C = TS<KP>::C;
-    const bool vec_ok = (n % C) == 0;
+template <int KP, bool TALL, typename S>
+__device__ __forceinline__ void slice_load_s(const void* base, int k, int N, int n, int l0, bool full,
+                                             float (&v)[KP][TS<KP>::VEC]) {
+  constexpr int VEC = TS<KP>::VEC, C = slice_vec<KP, TALL>();
+  const MUON_GLOBAL S* p = gmem(static_cast<const S*>(base));
+  if (full) {
+    if constexpr (!TALL) {
+#pragma unroll
+      for (int a = 0; a < KP; ++a)
+#pragma unroll
+        for (int e0 = 0; e0 < VEC; e0 += C) vload<S, C>(p + gidx<false>(a, l0 + e0, n), &v[a][e0]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e)
+#pragma unroll
+        for (int a0 = 0; a0 < KP; a0 += C) {
+          float t[C];
+          vload<S, C>(p + gidx<true>(a0, l0 + e, n), t);
+#pragma unroll
+          for (int i = 0; i < C; ++i) v[a0 + i][e] = t[i];
+        }
+    }
+  } else {
 #pragma unroll
     for (int a = 0; a < KP; ++a)
 #pragma unroll
-      for (int e0 = 0; e0 < VEC; e0 += C) {
-        const int avail = a < k ? clampi(N - (l0 + e0), 0, C) : 0;
-        float t[C];
-        load_run<C>(p, dt, static_cast<int64_t>(a) * n + l0 + e0, avail, vec_ok, t);
-#pragma unroll
-        for (int e = 0; e < C; ++e) v[a][e0 + e] = t[e];
-      }
-  } else {
-    constexpr int C = TS<KP>::CT;
-    const bool vec_ok = (n % C) == 0;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const int row = l0 + e;
-#pragma unroll
-      for (int a0 = 0; a0 < KP; a0 += C) {
-        const int avail = row < N ? clampi(k - a0, 0, C) : 0;
-        float t[C];
-        load_run<C>(p, dt, static_cast<int64_t>(row) * n + a0, avail, vec_ok, t);
-#pragma unroll
-        for (int i = 0; i < C; ++i) v[a0 + i][e] = t[i];
-      }
-    }
+      for (int e = 0; e < VEC; ++e)
+        v[a][e] = (a < k && l0 + e < N) ? to_f(p[gidx<TALL>(a, l0 + e, n)]) : 0.0f;
   }
 }
 
 template <int KP, bool TALL>
-__device__ __forceinline__ void slice_store(void* p, int32_t dt, int k, int N, int n, int l0,
-                                            const float (&v)[KP][TS<KP>::VEC]) {
-  constexpr int VEC = TS<KP>::VEC;
-  if constexpr (!TALL) {
-    constexpr int C = TS<KP>::C;
-    const bool vec_ok = (n % C) == 0;
+__device__ __forceinline__ void slice_load(const void* p, int32_t dt, int k, int N, int n, int l0, bool full,
+                                           float (&v)[KP][TS<KP>::VEC]) {
+  if (dt == DT_F32) slice_load_s<KP, TALL, float>(p, k, N, n, l0, full, v);
+  else slice_load_s<KP, TALL, uint16_t>(p, k, N, n, l0, full, v);
+}
+
+template <int KP, bool TALL, typename S>
+__device__ __forceinline__ void slice_store_s(void* base, int k, int N, int n, int l0, bool full,
+                                              const float (&v)[KP][TS<KP>::VEC]) {
+  constexpr int VEC = TS<KP>::VEC, C = slice_vec<KP, TALL>();
+  MUON_GLOBAL S* p = gmem(static_cast<S*>(base));
+  if (full) {
+    if constexpr (!TALL) {
+#pragma unroll
+      for (int a = 0; a < KP; ++a)
+#pragma unroll
+        for (int e0 = 0; e0 < VEC; e0 += C) vstore<S, C>(p + gidx<false>(a, l0 + e0, n), &v[a][e0]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e)
+#pragma unroll
+        for (int a0 = 0; a0 < KP; a0 += C) {
+          float t[C];
+#pragma unroll
+          for (int i = 0; i < C; ++i) t[i] = v[a0 + i][e];
+          vstore<S, C>(p + gidx<true>(a0, l0 + e, n), t);
+        }
+    }
+  } else {
 #pragma unroll
     for (int a = 0; a < KP; ++a)
 #pragma unroll
-      for (int e0 = 0; e0 < VEC; e0 += C) {
-        const int avail = a < k ? clampi(N - (l0 + e0), 0, C) : 0;
-        float t[C];
-#pragma unroll
-        for (int e = 0; e < C; ++e) t[e] = v[a][e0 + e];
-        if (avail > 0) store_run<C>(p, dt, static_cast<int64_t>(a) * n + l0 + e0, avail, vec_ok, t);
-      }
-  } else {
-    constexpr int C = TS<KP>::CT;
-    const bool vec_ok = (n % C) == 0;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const int row = l0 + e;
-#pragma unroll
-      for (int a0 = 0; a0 < KP; a0 += C) {
-        const int avail = row < N ? clampi(k - a0, 0, C) : 0;
-        float t[C];
-#pragma unroll
-        for (int i = 0; i < C; ++i) t[i] = v[a0 + i][e];
-        if (avail > 0) store_run<C>(p, dt, static_cast<int64_t>(row) * n + a0, avail, vec_ok, t);
-      }
-    }
+      for (int e = 0; e < VEC; ++e)
+        if (a < k && l0 + e < N) p[gidx<TALL>(a, l0 + e, n)] = from_f<S>(v[a][e]);
   }
+}
+
+template <int KP, bool TALL>
+__device__ __forceinline__ void slice_store(void* p, int32_t dt, int k, int N, int n, int l0, bool full,
+                                            const float (&v)[KP][TS<KP>::VEC]) {
+  if (dt == DT_F32) slice_store_s<KP, TALL, float>(p, k, N, n, l0, full, v);
+  else slice_store_s<KP, TALL, uint16_t>(p, k, N, n, l0, full, v);
 }
 
 // Pairwise tree over CNT in-register values (CNT a power of two).
@@ -209,104 +241,127 @@ __device__ __forceinline__ EnergyCache cache_of(const StepArgs& a, const MatDesc
 
 template <int KP>
 struct ThinSmem {
-  static constexpr int GP = TS<KP>::NPAIR < 36 ? TS<KP>::NPAIR : 36;   // Gram pairs per reduction group
-  double gred[NWV * 4][2][GP];     // 16-lane row sums of the Gram partials (wave, row)
+  static constexpr int GP = TS<KP>::NPAIR < 36 ? TS<KP>::NPAIR : 36;   // largest Gram pair group
+  union {                          // 16-lane row sums of a Gram pass (wave, row)
+    double d[NWV * 4][GP];
+    float f[NWV * 4][GP];
+  } gred;
   float red[NWV][KP];
   float fred[NWV];
   float rg[KP], dglob[KP];
   double sG[KP * KP], sG2[KP * KP];
-  double sA[KP * KP], sA2[KP * KP], sM[KP * KP], sQ[KP * KP], sT[KP * KP];
+  double sAA[2 * KP * KP];         // A and A2 of the k x k iteration; then the norm terms
+  double sM[KP * KP], sQ[KP * KP], sT[KP * KP];
   double nrm[2];
   float sQf[KP * KP];
   float post;
 };
 
-// Sum over each 16-lane row of the wave (the first four pairwise levels);
-// lanes 0, 16, 32, 48 then hold the row sums.
-template <typename T>
-__device__ __forceinline__ T row16_sum(T v) {
-  if constexpr (sizeof(T) == 4) {
-    v = v + dpp_f32<0xB1>(v);
-    v = v + dpp_f32<0x4E>(v);
-    v = v + dpp_f32<0x141>(v);
-    v = v + dpp_f32<0x140>(v);
-  } else {
-    v = v + dpp_f64<0xB1>(v);
-    v = v + dpp_f64<0x4E>(v);
-    v = v + dpp_f64<0x141>(v);
-    v = v + dpp_f64<0x140>(v);
-  }
-  return v;
+// 16-lane row sums of CNT values: four DPP levels (quad_perm [1,0,3,2],
+// [2,3,0,1], row_half_mirror, row_mirror) leave each 16-lane row's sum in all
+// of its lanes.  Values go through the levels four at a time, so that no DPP
+// read directly follows the write of its source.
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp_add(T v) {
+  if constexpr (sizeof(T) == 4) return v + dpp_f32<CTRL>(v);
+  else return v + dpp_f64<CTRL>(v);
 }
 
-// acc[i] += y_a * y_b and acc2[i] += (y_a w) * y_b for pair G*GP + i of one
-// position (pair rows are constants of the instantiation).
-template <typename TA, int KP, int P>
-__device__ __forceinline__ void pair_acc(const float (&y)[KP], TA w, TA& acc, TA& acc2, bool two) {
+template <typename T, int CNT>
+__device__ __forceinline__ void row16_sums(T (&v)[CNT]) {
+#pragma unroll
+  for (int i0 = 0; i0 < CNT; i0 += 4) {
+    constexpr int W = 4;
+#pragma unroll
+    for (int i = i0; i < i0 + W && i < CNT; ++i) v[i] = dpp_add<0xB1>(v[i]);
+#pragma unroll
+    for (int i = i0; i < i0 + W && i < CNT; ++i) v[i] = dpp_add<0x4E>(v[i]);
+#pragma unroll
+    for (int i = i0; i < i0 + W && i < CNT; ++i) v[i] = dpp_add<0x141>(v[i]);
+#pragma unroll
+    for (int i = i0; i < i0 + W && i < CNT; ++i) v[i] = dpp_add<0x140>(v[i]);
+  }
+}
+
+// acc += y_a * y_b (or (y_a w) * y_b when WEIGHTED) for pair P of one
+// position (the pair's rows are constants of the instantiation).
+template <typename TA, int KP, int P, bool WEIGHTED>
+__device__ __forceinline__ void pair_acc(const float (&y)[KP], TA w, TA& acc) {
   if constexpr (P < TS<KP>::NPAIR) {
     constexpr int a = pair_a(KP, P), b = pair_b(KP, P);
-    const TA ya = static_cast<TA>(y[a]), yb = static_cast<TA>(y[b]);
-    if constexpr (sizeof(TA) == 4) {
-      acc = __builtin_fmaf(ya, yb, acc);
-      if (two) acc2 = __builtin_fmaf(ya * w, yb, acc2);
-    } else {
-      acc = __builtin_fma(ya, yb, acc);
-      if (two) acc2 = __builtin_fma(ya * w, yb, acc2);
-    }
+    const TA ya = WEIGHTED ? static_cast<TA>(y[a]) * w : static_cast<TA>(y[a]);
+    const TA yb = static_cast<TA>(y[b]);
+    if constexpr (sizeof(TA) == 4) acc = __builtin_fmaf(ya, yb, acc);
+    else acc = __builtin_fma(ya, yb, acc);
   }
 }
 
-template <typename TA, int KP, int P0, int GP, int... Is>
-__device__ __forceinline__ void pair_group(const float (&y)[KP], TA w, TA (&acc)[GP], TA (&acc2)[GP], bool two,
+template <typename TA, int KP, int P0, bool WEIGHTED, int GP, int... Is>
+__device__ __forceinline__ void pair_group(const float (&y)[KP], TA w, TA (&acc)[GP],
                                            std::integer_sequence<int, Is...>) {
-  (pair_acc<TA, KP, P0 + Is>(y, w, acc[Is], acc2[Is], two), ...);
+  (pair_acc<TA, KP, P0 + Is, WEIGHTED>(y, w, acc[Is]), ...);
 }
 
-// Gram partials of this slice: sum over the slice's positions of y_a y_b
-// (and of y_a d_loc^2 y_b when `two`), pairs in groups of GP: per-thread sums
-// over its VEC positions in TA, the 16-lane row sums (DPP), then the 16 row
-// sums of the 4 waves added in a fixed order in double.
-template <typename TA, int KP, int G, int NG>
-__device__ __forceinline__ void gram_slice(const float (&y)[KP][TS<KP>::VEC], const float (&dl)[TS<KP>::VEC],
-                                           bool two, double* out, double* out2, ThinSmem<KP>& sm) {
-  if constexpr (G < NG) {
-    constexpr int VEC = TS<KP>::VEC, NPAIR = TS<KP>::NPAIR, GP = ThinSmem<KP>::GP;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    TA acc[GP], acc2[GP];
+// Gram pairs reduced per pass: GP accumulators per thread stay live.
+template <int KP, typename TA>
+constexpr int gram_group() {
+  constexpr int cap = sizeof(TA) == 4 ? 36 : 18;
+  return TS<KP>::NPAIR < cap ? TS<KP>::NPAIR : cap;
+}
+
+// Pairs [P0, P0 + GP) of the slice's Gram (plain, or d_loc^2 weighted):
+// per-thread sums over its VEC positions in TA, the 16-lane row sums (DPP),
+// then the 16 row sums of the 4 waves added in a fixed order in double.
+template <typename TA, int KP, int P0, bool WEIGHTED>
+__device__ __forceinline__ void gram_pass(const float (&y)[KP][TS<KP>::VEC], const float (&dl)[TS<KP>::VEC],
+                                          MUON_GLOBAL double* out, ThinSmem<KP>& sm) {
+  constexpr int VEC = TS<KP>::VEC, NPAIR = TS<KP>::NPAIR, GP = gram_group<KP, TA>();
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  TA acc[GP];
 #pragma unroll
-    for (int i = 0; i < GP; ++i) { acc[i] = TA(0); acc2[i] = TA(0); }
+  for (int i = 0; i < GP; ++i) acc[i] = TA(0);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      float col[KP];
+  for (int e = 0; e < VEC; ++e) {
+    float col[KP];
 #pragma unroll
-      for (int a = 0; a < KP; ++a) col[a] = y[a][e];
-      const TA w = static_cast<TA>(dl[e]) * static_cast<TA>(dl[e]);
-      pair_group<TA, KP, G * GP, GP>(col, w, acc, acc2, two, std::make_integer_sequence<int, GP>{});
-    }
+    for (int a = 0; a < KP; ++a) col[a] = y[a][e];
+    const TA w = static_cast<TA>(dl[e]) * static_cast<TA>(dl[e]);
+    pair_group<TA, KP, P0, WEIGHTED>(col, w, acc, std::make_integer_sequence<int, GP>{});
+  }
+  row16_sums(acc);
+  if ((lane & 15) == 0) {
+    const int row = wave * 4 + (lane >> 4);
 #pragma unroll
     for (int i = 0; i < GP; ++i) {
-      const TA r1 = row16_sum(acc[i]);
-      const TA r2 = two ? row16_sum(acc2[i]) : TA(0);
-      if ((lane & 15) == 0) {
-        sm.gred[wave * 4 + (lane >> 4)][0][i] = static_cast<double>(r1);
-        sm.gred[wave * 4 + (lane >> 4)][1][i] = static_cast<double>(r2);
-      }
+      if constexpr (sizeof(TA) == 4) sm.gred.f[row][i] = acc[i];
+      else sm.gred.d[row][i] = acc[i];
     }
-    __syncthreads();
-    for (int i = tid; i < GP; i += TT) {
-      const int p = G * GP + i;
-      if (p < NPAIR) {
-        double s1 = 0.0, s2 = 0.0;
+  }
+  lds_barrier();
+  for (int i = tid; i < GP; i += TT) {
+    if (P0 + i < NPAIR) {
+      double s1 = 0.0;
 #pragma unroll
-        for (int r = 0; r < NWV * 4; ++r) {
-          s1 = s1 + sm.gred[r][0][i];
-          s2 = s2 + sm.gred[r][1][i];
-        }
-        out[p] = s1;
-        if (two) out2[p] = s2;
+      for (int r = 0; r < NWV * 4; ++r) {
+        if constexpr (sizeof(TA) == 4) s1 = s1 + static_cast<double>(sm.gred.f[r][i]);
+        else s1 = s1 + sm.gred.d[r][i];
       }
+      out[P0 + i] = s1;
     }
-    __syncthreads();
+  }
+  lds_barrier();
+}
+
+// Gram partials of this slice, pair groups G.. of both Grams (the weighted
+// one when `two`).
+template <typename TA, int KP, int G, int NG>
+__device__ __forceinline__ void gram_slice(const float (&y)[KP][TS<KP>::VEC], const float (&dl)[TS<KP>::VEC],
+                                           bool two, MUON_GLOBAL double* out, MUON_GLOBAL double* out2,
+                                           ThinSmem<KP>& sm) {
+  if constexpr (G < NG) {
+    constexpr int P0 = G * gram_group<KP, TA>();
+    gram_pass<TA, KP, P0, false>(y, dl, out, sm);
+    if (two) gram_pass<TA, KP, P0, true>(y, dl, out2, sm);
     gram_slice<TA, KP, G + 1, NG>(y, dl, two, out, out2, sm);
   }
 }
@@ -325,7 +380,7 @@ __device__ __forceinline__ void energies_to_cache(const float (&v)[KP][TS<KP>::V
     for (int a = 0; a < KP; ++a) col[a] = v[a][e] * v[a][e];
     const float pe = tree<KP>(col);
     if (l0 + e < d.N) {
-      c.pos[l0 + e] = pe;
+      gmem(c.pos)[l0 + e] = pe;
       lmax = fmaxf(lmax, pe);
     }
   }
@@ -339,20 +394,20 @@ __device__ __forceinline__ void energies_to_cache(const float (&v)[KP][TS<KP>::V
   }
   lmax = wave_max(lmax);
   if (lane == 0) sm.fred[wave] = lmax;
-  __syncthreads();
+  lds_barrier();
   if (tid < KP) {
     float w4[NWV];
 #pragma unroll
     for (int w = 0; w < NWV; ++w) w4[w] = sm.red[w][tid];
-    c.part[static_cast<int64_t>(s) * KP + tid] = tree<NWV>(w4);
+    gmem(c.part)[static_cast<int64_t>(s) * KP + tid] = tree<NWV>(w4);
   }
   if (tid == 0) {
     float m = sm.fred[0];
 #pragma unroll
     for (int w = 1; w < NWV; ++w) m = fmaxf(m, sm.fred[w]);
-    c.smax[s] = m;
+    gmem(c.smax)[s] = m;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // ---------------------------------------------------------------------------
@@ -364,7 +419,7 @@ __device__ __forceinline__ void energy_body(const StepArgs& args, const MatDesc&
   constexpr int VEC = TS<KP>::VEC, L = TS<KP>::L;
   const int l0 = s * L + threadIdx.x * VEC;
   float y[KP][VEC];
-  slice_load<KP, TALL>(d.mom, args.mom_dt, d.k, d.N, d.n, l0, y);
+  slice_load<KP, TALL>(d.mom, args.mom_dt, d.k, d.N, d.n, l0, slice_full<KP, TALL>(d.k, d.N, d.n, s), y);
   energies_to_cache<KP>(y, d, s, l0, cache_of(args, d, parity), sm);
 }
 
@@ -380,7 +435,8 @@ __global__ __launch_bounds__(TT) void k_thin_energy(StepArgs args, const Tile* _
 // ---------------------------------------------------------------------------
 // Pass A
 // ---------------------------------------------------------------------------
-template <int KP, bool TALL>
+// TA: accumulation type of the per-thread Gram sums.
+template <int KP, bool TALL, typename TA>
 __device__ __forceinline__ void pass_a_body(const StepArgs& args, const MatDesc& d, int s, int parity,
                                             ThinSmem<KP>& sm) {
   constexpr int VEC = TS<KP>::VEC, L = TS<KP>::L, NPAIR = TS<KP>::NPAIR;
@@ -389,26 +445,33 @@ __device__ __forceinline__ void pass_a_body(const StepArgs& args, const MatDesc&
   const int l0 = s * L + tid * VEC;
   const bool dimuon = args.dimuon != 0;
 
+  // The energy cache loads go first: the factors are computed while the
+  // slice is still loading.
+  const EnergyCache cin = cache_of(args, d, parity);
+  float part8[8], smax = 0.0f, pe[VEC];
+  if (dimuon) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) part8[j] = (tid < k && j < d.S) ? gmem(cin.part)[j * KP + tid] : 0.0f;
+    if (tid < d.S) smax = gmem(cin.smax)[tid];   // S <= TT
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) pe[e] = (l0 + e < N) ? gmem(cin.pos)[l0 + e] : 0.0f;
+  }
+
+  const bool full = slice_full<KP, TALL>(k, N, n, s);
   float y[KP][VEC];   // M_{t-1}, then M_t, then Y
   float g[KP][VEC];
-  slice_load<KP, TALL>(d.mom, args.mom_dt, k, N, n, l0, y);
-  slice_load<KP, TALL>(d.g, args.g_dt, k, N, n, l0, g);
+  slice_load<KP, TALL>(d.mom, args.mom_dt, k, N, n, l0, full, y);
+  slice_load<KP, TALL>(d.g, args.g_dt, k, N, n, l0, full, g);
 
   // ---- Dimuon factors from the energies of M_{t-1} --------------------------
   float dloc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) dloc[e] = 1.0f;
   if (dimuon) {
-    const EnergyCache cin = cache_of(args, d, parity);
-    if (tid < KP) sm.rg[tid] = tid < k ? pairwise_strided(cin.part + tid, d.S, KP) : 0.0f;
-    float m = 0.0f;
-    for (int i = tid; i < d.S; i += TT) m = fmaxf(m, cin.smax[i]);
-    m = wave_max(m);
+    if (tid < KP) sm.rg[tid] = tid < k ? pairwise_strided8(part8, cin.part + tid, d.S, KP) : 0.0f;
+    const float m = wave_max(smax);
     if (lane == 0) sm.fred[wave] = m;
-    float pe[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) pe[e] = (l0 + e < N) ? cin.pos[l0 + e] : 0.0f;
-    __syncthreads();
+    lds_barrier();
     float emax_loc = sm.fred[0];
 #pragma unroll
     for (int w = 1; w < NWV; ++w) emax_loc = fmaxf(emax_loc, sm.fred[w]);
@@ -422,21 +485,20 @@ __device__ __forceinline__ void pass_a_body(const StepArgs& args, const MatDesc&
       // wide: R = Gram-side (k rows), C = per position (N); tall: R per position, C Gram-side.
       float* glob_out = d.tall ? d.energy_out + d.m : d.energy_out;
       float* loc_out = d.tall ? d.energy_out : d.energy_out + d.m;
-      if (s == 0 && tid < k) glob_out[tid] = sm.rg[tid];
+      if (s == 0 && tid < k) gmem(glob_out)[tid] = sm.rg[tid];
 #pragma unroll
       for (int e = 0; e < VEC; ++e)
-        if (l0 + e < N) loc_out[l0 + e] = pe[e];
+        if (l0 + e < N) gmem(loc_out)[l0 + e] = pe[e];
     }
-    __syncthreads();   // dglob visible; rg / fred reads done before reuse
+    lds_barrier();   // dglob visible; rg / fred reads done before reuse
   }
 
-  // ---- momentum; energies of M_t for the next step ---------------------------
+  // ---- momentum ----------------------------------------------------------------
 #pragma unroll
   for (int a = 0; a < KP; ++a)
 #pragma unroll
     for (int e = 0; e < VEC; ++e) y[a][e] = momentum_value(args.mu, y[a][e], g[a][e], args.mom_dt);
-  slice_store<KP, TALL>(d.mom, args.mom_dt, k, N, n, l0, y);
-  if (dimuon) energies_to_cache<KP>(y, d, s, l0, cache_of(args, d, parity ^ 1), sm);
+  slice_store<KP, TALL>(d.mom, args.mom_dt, k, N, n, l0, full, y);
 
   // ---- Y = D_glob V D_loc -----------------------------------------------------
   if (args.nesterov) {
@@ -450,37 +512,44 @@ __device__ __forceinline__ void pass_a_body(const StepArgs& args, const MatDesc&
     for (int a = 0; a < KP; ++a)
 #pragma unroll
       for (int e = 0; e < VEC; ++e) y[a][e] = (sm.dglob[a] * y[a][e]) * dloc[e];
-    float* tdl = reinterpret_cast<float*>(args.ws + d.tdl_off);
+    MUON_GLOBAL float* tdl = gmem(reinterpret_cast<float*>(args.ws + d.tdl_off));
 #pragma unroll
     for (int e = 0; e < VEC; ++e)
       if (l0 + e < N) tdl[l0 + e] = dloc[e];
-    if (s == 0 && tid < KP) reinterpret_cast<float*>(args.ws + d.tdg_off)[tid] = sm.dglob[tid];
+    if (s == 0 && tid < KP) gmem(reinterpret_cast<float*>(args.ws + d.tdg_off))[tid] = sm.dglob[tid];
   }
 
   // ---- Gram partials of the slice ---------------------------------------------
   {
-    constexpr int GP = ThinSmem<KP>::GP, NG = (NPAIR + GP - 1) / GP;
-    double* tg = reinterpret_cast<double*>(args.ws + d.tg_off) + static_cast<int64_t>(s) * NPAIR;
-    double* tg2 = reinterpret_cast<double*>(args.ws + d.tg2_off) + static_cast<int64_t>(s) * NPAIR;
-    // The orthogonaliser's precision sets the Gram's: float32 sums when the
-    // NS products are bf16, float64 in fp32 mode.
-    if (args.ns_dt == DT_BF16) gram_slice<float, KP, 0, NG>(y, dloc, dimuon, tg, tg2, sm);
-    else gram_slice<double, KP, 0, NG>(y, dloc, dimuon, tg, tg2, sm);
+    constexpr int GP = gram_group<KP, TA>(), NG = (NPAIR + GP - 1) / GP;
+    MUON_GLOBAL double* tg = gmem(reinterpret_cast<double*>(args.ws + d.tg_off)) + static_cast<int64_t>(s) * NPAIR;
+    MUON_GLOBAL double* tg2 = gmem(reinterpret_cast<double*>(args.ws + d.tg2_off)) + static_cast<int64_t>(s) * NPAIR;
+    gram_slice<TA, KP, 0, NG>(y, dloc, dimuon, tg, tg2, sm);
   }
 }
 
-template <int KP>
-__global__ __launch_bounds__(TT) void k_thin_a(StepArgs args, const Tile* __restrict__ tiles, int parity) {
+// The orthogonaliser's precision sets the Gram's: float32 per-thread sums
+// when the Newton-Schulz products are bf16, float64 in fp32 mode.
+template <int KP, typename TA>
+__global__ __launch_bounds__(TT, 4) void k_thin_a(StepArgs args, const Tile* __restrict__ tiles, int parity) {
   __shared__ ThinSmem<KP> sm;
   const Tile t = tiles[blockIdx.x];
   const MatDesc& d = args.desc[t.mat];
-  if (d.tall) pass_a_body<KP, true>(args, d, t.ti, parity, sm);
-  else pass_a_body<KP, false>(args, d, t.ti, parity, sm);
+  if (d.tall) pass_a_body<KP, true, TA>(args, d, t.ti, parity, sm);
+  else pass_a_body<KP, false, TA>(args, d, t.ti, parity, sm);
 }
 
 // ---------------------------------------------------------------------------
 // Pass B
 // ---------------------------------------------------------------------------
+// Orders the LDS accesses of one wave (a wave's LDS operations complete in
+// order; this keeps the compiler from moving them across).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 // k x k iteration in fp64 on LDS matrices (all symmetric): A <- G / nu^2,
 // Q <- I; per step M = aI + bA + cA^2, Q <- M Q, A <- M A M.  Small KP runs on
 // one wave with one entry per lane (a wave's LDS operations complete in
@@ -490,15 +559,15 @@ __device__ __forceinline__ void kxk_wave(ThinSmem<KP>& sm, double inv_nu2, int n
   const int lane = threadIdx.x & 63;
   const bool own = lane < KP * KP;
   const int r = lane / KP, c = lane % KP;
-  double* A = sm.sA;
-  double* A2 = sm.sA2;
+  double* A = sm.sAA;
+  double* A2 = sm.sAA + KP * KP;
   double* Q = sm.sQ;
   double* T = sm.sT;
   if (own) {
     A[lane] = sm.sG[lane] * inv_nu2;
     Q[lane] = (r == c) ? 1.0 : 0.0;
   }
-  __builtin_amdgcn_wave_barrier();
+  wave_lds_sync();
   for (int t = 0; t < ns_steps; ++t) {
     const double ca = cf.c[t].a, cb = cf.c[t].b, cc = cf.c[t].c;
     if (own) {
@@ -507,7 +576,7 @@ __device__ __forceinline__ void kxk_wave(ThinSmem<KP>& sm, double inv_nu2, int n
       for (int q = 0; q < KP; ++q) acc = __builtin_fma(A[r * KP + q], A[q * KP + c], acc);
       sm.sM[lane] = ((r == c) ? ca : 0.0) + cb * A[lane] + cc * acc;
     }
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_sync();
     if (own) {
       double q1 = 0.0, t2 = 0.0;
 #pragma unroll
@@ -518,7 +587,7 @@ __device__ __forceinline__ void kxk_wave(ThinSmem<KP>& sm, double inv_nu2, int n
       T[lane] = q1;
       A2[lane] = t2;
     }
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_sync();
     if (own) {
       double a2 = 0.0;
 #pragma unroll
@@ -526,10 +595,10 @@ __device__ __forceinline__ void kxk_wave(ThinSmem<KP>& sm, double inv_nu2, int n
       A[lane] = a2;
     }
     double* sw = Q; Q = T; T = sw;
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_sync();
   }
   if (own && Q != sm.sQ) sm.sQ[lane] = Q[lane];
-  __builtin_amdgcn_wave_barrier();
+  wave_lds_sync();
 }
 
 template <int KP>
@@ -541,19 +610,19 @@ __device__ __forceinline__ void mm64(double* C, const double* X, const double* Y
     for (int q = 0; q < KP; ++q) s = __builtin_fma(X[r * KP + q], Y[q * KP + c], s);
     C[e] = s;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 template <int KP>
 __device__ __forceinline__ void kxk_block(ThinSmem<KP>& sm, double inv_nu2, int ns_steps, const ThinCoeffs& cf) {
   const int tid = threadIdx.x;
   for (int e = tid; e < KP * KP; e += TT) {
-    sm.sA[e] = sm.sG[e] * inv_nu2;
+    sm.sAA[e] = sm.sG[e] * inv_nu2;
     sm.sQ[e] = (e / KP == e % KP) ? 1.0 : 0.0;
   }
-  __syncthreads();
-  double* A = sm.sA;
-  double* A2 = sm.sA2;
+  lds_barrier();
+  double* A = sm.sAA;
+  double* A2 = sm.sAA + KP * KP;
   double* Q = sm.sQ;
   double* T = sm.sT;
   for (int t = 0; t < ns_steps; ++t) {
@@ -563,7 +632,7 @@ __device__ __forceinline__ void kxk_block(ThinSmem<KP>& sm, double inv_nu2, int 
       const double diag = (e / KP == e % KP) ? ca : 0.0;
       sm.sM[e] = diag + cb * A[e] + cc * A2[e];
     }
-    __syncthreads();
+    lds_barrier();
     mm64<KP>(T, sm.sM, Q);
     double* sw = Q; Q = T; T = sw;
     mm64<KP>(A2, sm.sM, A);
@@ -571,100 +640,147 @@ __device__ __forceinline__ void kxk_block(ThinSmem<KP>& sm, double inv_nu2, int 
   }
   if (Q != sm.sQ)
     for (int e = tid; e < KP * KP; e += TT) sm.sQ[e] = Q[e];
-  __syncthreads();
+  lds_barrier();
 }
 
-// ||Z||^2 = sum_a (Q G Q^T)_aa / nu^2 and ||D_R Z D_C||^2 = sum_a d_a^2 (Q G2 Q^T)_aa / nu^2
-// (Q symmetric).  Thread a < KP computes row a's term with one code path for
-// both, so equal Grams and unit weights give bit-equal norms; thread 0 sums
-// the KP terms in order.
+// ||Z||^2 = sum_a (Q G Q^T)_aa / nu^2 and ||D_R Z D_C||^2 = sum_a d_a^2 (Q G2 Q^T)_aa / nu^2.
+// Entry (a, c) of each product term t_ac = (Q H)_ac Q_ac is one thread's;
+// row a's terms are then summed in order, and the rows in order.  Both norms
+// take the same code path, so equal Grams and unit weights give bit-equal
+// norms.
 template <int KP>
 __device__ __forceinline__ void gram_norms(ThinSmem<KP>& sm, double inv_nu) {
   const int tid = threadIdx.x;
-  double* terms = sm.sT;   // free after the k x k iteration
+  double* terms = sm.sAA;   // free after the k x k iteration
+  for (int e = tid; e < 2 * KP * KP; e += TT) {
+    const int which = e / (KP * KP), a = (e / KP) % KP, c = e % KP;
+    const double* H = which ? sm.sG2 : sm.sG;
+    double t = 0.0;
+#pragma unroll
+    for (int b = 0; b < KP; ++b) t = __builtin_fma(sm.sQ[a * KP + b], H[b * KP + c], t);
+    terms[e] = t * sm.sQ[a * KP + c];
+  }
+  lds_barrier();
+  double* rows = sm.sM;
   if (tid < 2 * KP) {
     const int which = tid / KP, a = tid % KP;
-    const double* H = which ? sm.sG2 : sm.sG;
-    double da = 0.0;
-    for (int c = 0; c < KP; ++c) {
-      double t = 0.0;
-#pragma unroll 8
-      for (int b = 0; b < KP; ++b) t = __builtin_fma(sm.sQ[a * KP + b], H[b * KP + c], t);
-      da = __builtin_fma(t, sm.sQ[a * KP + c], da);
-    }
+    double r = 0.0;
+    for (int c = 0; c < KP; ++c) r = r + terms[tid * KP + c];
     const double w = which ? static_cast<double>(sm.dglob[a]) * static_cast<double>(sm.dglob[a]) : 1.0;
-    terms[which * KP + a] = w * (da * inv_nu * inv_nu);
+    rows[tid] = w * (r * inv_nu * inv_nu);
   }
-  __syncthreads();
+  lds_barrier();
   if (tid < 2) {
     double tot = 0.0;
-    for (int a = 0; a < KP; ++a) tot = tot + terms[tid * KP + a];
+    for (int a = 0; a < KP; ++a) tot = tot + rows[tid * KP + a];
     sm.nrm[tid] = tot;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 template <int KP, bool TALL>
 __device__ __forceinline__ void pass_b_body(const StepArgs& args, const MatDesc& d, int s, int ns_steps,
-                                            const ThinCoeffs& cf, ThinSmem<KP>& sm) {
+                                            const ThinCoeffs& cf, int parity, ThinSmem<KP>& sm) {
   constexpr int VEC = TS<KP>::VEC, L = TS<KP>::L, NPAIR = TS<KP>::NPAIR;
   const int tid = threadIdx.x, wave = tid >> 6;
   const int k = d.k, N = d.N, n = d.n;
   const int l0 = s * L + tid * VEC;
   const bool dimuon = args.dimuon != 0;
 
-  // Loads first: they are in flight during the k x k work.
+  // The k x k work waits only on the Gram partials; the slice stays in flight
+  // meanwhile.  For KP <= 8 the partials and the iteration belong to wave 0,
+  // which runs them before issuing its own share of the slice loads (a wave
+  // issues in order, and issuing loads stalls while the memory queue is
+  // full); for larger KP every thread loads its partials first.
+  const MUON_GLOBAL double* tg = gmem(reinterpret_cast<const double*>(args.ws + d.tg_off));
+  const MUON_GLOBAL double* tg2 = gmem(reinterpret_cast<const double*>(args.ws + d.tg2_off));
+  constexpr int PB = 8;   // partial loads in flight per thread and round
+  double v1[PB], v2[PB];
+  auto load_partials = [&](int p, int i0) {
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+      const bool in = p < NPAIR && i0 + j < d.S;
+      const int64_t at = static_cast<int64_t>(i0 + j) * NPAIR + p;
+      v1[j] = in ? tg[at] : 0.0;
+      v2[j] = (in && dimuon) ? tg2[at] : 0.0;
+    }
+  };
+  // Sums the partials of pairs tid, tid + TT, ... in slice order into sG, sG2;
+  // the first round of pair tid is already in v1, v2.
+  auto sum_partials = [&]() {
+    for (int p = tid; p < NPAIR; p += TT) {
+      double a1 = 0.0, a2 = 0.0;
+      for (int i0 = 0; i0 < d.S; i0 += PB) {
+        if (i0 > 0 || p != tid) load_partials(p, i0);
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+          a1 = a1 + v1[j];
+          a2 = a2 + v2[j];
+        }
+      }
+      const int a = pair_a(KP, p), b = pair_b(KP, p);
+      sm.sG[a * KP + b] = a1;
+      sm.sG[b * KP + a] = a1;
+      sm.sG2[a * KP + b] = a2;
+      sm.sG2[b * KP + a] = a2;
+    }
+  };
+  auto inv_norm = [&]() {
+    double nu2 = 0.0;
+    for (int a = 0; a < KP; ++a) nu2 = nu2 + sm.sG[a * KP + a];
+    return (nu2 == 0.0) ? 0.0 : 1.0 / sqrt(nu2);
+  };
+
+  if constexpr (KP <= 8) {
+    if (wave == 0) {
+      load_partials(tid, 0);
+      sum_partials();
+      wave_lds_sync();
+      const double in0 = inv_norm();
+      kxk_wave<KP>(sm, in0 * in0, ns_steps, cf);
+    }
+  } else {
+    load_partials(tid, 0);
+  }
+
+  const float dg = (dimuon && tid < KP) ? gmem(reinterpret_cast<const float*>(args.ws + d.tdg_off))[tid] : 1.0f;
   float y[KP][VEC];   // M_t, then Y, then O
   float w[KP][VEC];   // W
   float g[KP][VEC];   // G (Nesterov only)
-  slice_load<KP, TALL>(d.mom, args.mom_dt, k, N, n, l0, y);
-  slice_load<KP, TALL>(d.w, args.w_dt, k, N, n, l0, w);
-  if (args.nesterov) slice_load<KP, TALL>(d.g, args.g_dt, k, N, n, l0, g);
+  const bool full = slice_full<KP, TALL>(k, N, n, s);
+  slice_load<KP, TALL>(d.mom, args.mom_dt, k, N, n, l0, full, y);
+  slice_load<KP, TALL>(d.w, args.w_dt, k, N, n, l0, full, w);
+  if (args.nesterov) slice_load<KP, TALL>(d.g, args.g_dt, k, N, n, l0, full, g);
   float dloc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) dloc[e] = 1.0f;
   if (dimuon) {
-    const float* tdl = reinterpret_cast<const float*>(args.ws + d.tdl_off);
+    const MUON_GLOBAL float* tdl = gmem(reinterpret_cast<const float*>(args.ws + d.tdl_off));
 #pragma unroll
     for (int e = 0; e < VEC; ++e) dloc[e] = (l0 + e < N) ? tdl[l0 + e] : 1.0f;
-    if (tid < KP) sm.dglob[tid] = reinterpret_cast<const float*>(args.ws + d.tdg_off)[tid];
   }
 
-  // ---- Gram: the slice partials summed in slice order -------------------------
-  const double* tg = reinterpret_cast<const double*>(args.ws + d.tg_off);
-  const double* tg2 = reinterpret_cast<const double*>(args.ws + d.tg2_off);
-  for (int p = tid; p < NPAIR; p += TT) {
-    double a1 = 0.0, a2 = 0.0;
-    for (int i = 0; i < d.S; ++i) {
-      a1 = a1 + tg[static_cast<int64_t>(i) * NPAIR + p];
-      if (dimuon) a2 = a2 + tg2[static_cast<int64_t>(i) * NPAIR + p];
-    }
-    const int a = pair_a(KP, p), b = pair_b(KP, p);
-    sm.sG[a * KP + b] = a1;
-    sm.sG[b * KP + a] = a1;
-    sm.sG2[a * KP + b] = a2;
-    sm.sG2[b * KP + a] = a2;
-  }
-  __syncthreads();
-
-  // ---- k x k iteration, norms ----------------------------------------------
-  double nu2 = 0.0;
-  for (int a = 0; a < KP; ++a) nu2 = nu2 + sm.sG[a * KP + a];
-  const double inv_nu = (nu2 == 0.0) ? 0.0 : 1.0 / sqrt(nu2);
-  if constexpr (KP <= 8) {
-    if (wave == 0) kxk_wave<KP>(sm, inv_nu * inv_nu, ns_steps, cf);
-    __syncthreads();
+  if constexpr (KP > 8) {
+    sum_partials();
+    lds_barrier();
+    const double in0 = inv_norm();
+    kxk_block<KP>(sm, in0 * in0, ns_steps, cf);
   } else {
-    kxk_block<KP>(sm, inv_nu * inv_nu, ns_steps, cf);
+    lds_barrier();
   }
+  const double inv_nu = inv_norm();
   for (int e = tid; e < KP * KP; e += TT) sm.sQf[e] = static_cast<float>(sm.sQ[e] * inv_nu);
+  if (tid < KP) sm.dglob[tid] = dg;   // read after the next barrier
   if (dimuon) {
     gram_norms<KP>(sm, inv_nu);
     if (tid == 0) sm.post = (sm.nrm[1] == 0.0) ? 0.0f : static_cast<float>(sqrt(sm.nrm[0]) / sqrt(sm.nrm[1]));
   } else if (tid == 0) {
     sm.post = 1.0f;
   }
-  __syncthreads();
+  lds_barrier();
+
+  // ---- energies of M_t for the next step's conditioning --------------------
+  if (dimuon) energies_to_cache<KP>(y, d, s, l0, cache_of(args, d, parity ^ 1), sm);
 
   // ---- Y, Z = Qs Y, O, update ------------------------------------------------
   if (args.nesterov) {
@@ -703,18 +819,18 @@ __device__ __forceinline__ void pass_b_body(const StepArgs& args, const MatDesc&
         w[a][e] = __builtin_fmaf(-args.lr, upd, w[a][e]);
       }
   }
-  slice_store<KP, TALL>(d.w, args.w_dt, k, N, n, l0, w);
-  if (d.o_out) slice_store<KP, TALL>(d.o_out, DT_F32, k, N, n, l0, y);
+  slice_store<KP, TALL>(d.w, args.w_dt, k, N, n, l0, full, w);
+  if (d.o_out) slice_store<KP, TALL>(d.o_out, DT_F32, k, N, n, l0, full, y);
 }
 
 template <int KP>
 __global__ __launch_bounds__(TT) void k_thin_b(StepArgs args, const Tile* __restrict__ tiles, int ns_steps,
-                                                ThinCoeffs cf) {
+                                                ThinCoeffs cf, int parity) {
   __shared__ ThinSmem<KP> sm;
   const Tile t = tiles[blockIdx.x];
   const MatDesc& d = args.desc[t.mat];
-  if (d.tall) pass_b_body<KP, true>(args, d, t.ti, ns_steps, cf, sm);
-  else pass_b_body<KP, false>(args, d, t.ti, ns_steps, cf, sm);
+  if (d.tall) pass_b_body<KP, true>(args, d, t.ti, ns_steps, cf, parity, sm);
+  else pass_b_body<KP, false>(args, d, t.ti, ns_steps, cf, parity, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -737,18 +853,32 @@ hipError_t launch_thin_energy(const StepArgs& a, const Tile* tiles, int n, int k
   return hipGetLastError();
 }
 
-hipError_t launch_thin_a(const StepArgs& a, const Tile* tiles, int n, int kp, int parity, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  MUON_THIN_DISPATCH(k_thin_a, a, tiles, parity)
+template <typename TA>
+hipError_t launch_thin_a_t(const StepArgs& a, const Tile* tiles, int n, int kp, int parity, hipStream_t s) {
+  switch (kp) {
+    case 1: hipLaunchKernelGGL((k_thin_a<1, TA>), dim3(n), dim3(TT), 0, s, a, tiles, parity); break;
+    case 2: hipLaunchKernelGGL((k_thin_a<2, TA>), dim3(n), dim3(TT), 0, s, a, tiles, parity); break;
+    case 4: hipLaunchKernelGGL((k_thin_a<4, TA>), dim3(n), dim3(TT), 0, s, a, tiles, parity); break;
+    case 8: hipLaunchKernelGGL((k_thin_a<8, TA>), dim3(n), dim3(TT), 0, s, a, tiles, parity); break;
+    case 16: hipLaunchKernelGGL((k_thin_a<16, TA>), dim3(n), dim3(TT), 0, s, a, tiles, parity); break;
+    case 32: hipLaunchKernelGGL((k_thin_a<32, TA>), dim3(n), dim3(TT), 0, s, a, tiles, parity); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
+hipError_t launch_thin_a(const StepArgs& a, const Tile* tiles, int n, int kp, int parity, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (a.ns_dt == DT_BF16) return launch_thin_a_t<float>(a, tiles, n, kp, parity, s);
+  return launch_thin_a_t<double>(a, tiles, n, kp, parity, s);
+}
+
 hipError_t launch_thin_b(const StepArgs& a, const Tile* tiles, int n, int kp, int ns_steps, const Coeffs* cf,
-                         hipStream_t s) {
+                         int parity, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   ThinCoeffs c{};
   for (int t = 0; t < ns_steps && t < kMaxSteps; ++t) c.c[t] = cf[t];
-  MUON_THIN_DISPATCH(k_thin_b, a, tiles, ns_steps, c)
+  MUON_THIN_DISPATCH(k_thin_b, a, tiles, ns_steps, c, parity)
   return hipGetLastError();
 }
 
