@@ -67,14 +67,17 @@ bool finite(float x) { return std::isfinite(x); }
 // ---------------------------------------------------------------------------
 struct Plan {
   std::vector<MatDesc> desc;
-  std::vector<Tile> k1, k3, syrk, comb, k5;
+  std::vector<Tile> k1, k3, k5, cond;
+  // GEMM tile lists, one launch each; bm x bn tiles (symmetric products: square)
+  struct GemmList { int bm, bn; std::vector<Tile> tiles; size_t off; };
+  std::vector<GemmList> syrk, comb;
   std::vector<uint16_t> gen;
   // thin matrices grouped by padded Gram side KP; one tile (matrix, slice)
   // per workgroup, one launch per phase and KP
   struct ThinGroup { int kp; std::vector<Tile> tiles; size_t off; };
   std::vector<ThinGroup> thin;
   // byte offsets in the workspace
-  size_t desc_off = 0, scal_off = 0, k1_off = 0, k3_off = 0, syrk_off = 0, comb_off = 0, k5_off = 0, gen_off = 0;
+  size_t desc_off = 0, scal_off = 0, k1_off = 0, k3_off = 0, k5_off = 0, cond_off = 0, gen_off = 0;
   size_t table_bytes = 0;   // uploaded prefix of the workspace
   size_t total_bytes = 0;   // whole workspace
   std::vector<unsigned char> table;
@@ -170,6 +173,69 @@ size_t put(std::vector<unsigned char>& buf, size_t off, const std::vector<T>& v)
   return off;
 }
 
+// GEMM tiles of the general path.  A 256-wide tile side is possible where
+// the padded side is a multiple of 256; those kernels run one workgroup per
+// CU, the 128 x 128 kernel two.  For each product kind the batch takes the
+// big tiles where they fit, unless the estimated time with 128 x 128 tiles
+// everywhere is lower (few big tiles leave CUs idle in the last round).
+// Within a matrix, tiles are listed in groups of four tile rows, column by
+// column, so that the workgroups running at once share operand panels.
+constexpr int kCUs = 256;
+constexpr double kSmallTileEff = 0.6;   // 128 x 128 kernel efficiency relative to the big tiles
+
+void add_tiles(std::vector<Tile>& out, uint16_t mat, int rows, int cols, bool upper) {
+  constexpr int kGroup = 4;
+  for (int g0 = 0; g0 < rows; g0 += kGroup)
+    for (int tj = 0; tj < cols; ++tj)
+      for (int ti = g0; ti < std::min(rows, g0 + kGroup); ++ti)
+        if (!upper || ti <= tj) out.push_back({mat, static_cast<uint16_t>(ti), static_cast<uint16_t>(tj), 0});
+}
+
+void plan_gemm_tiles(Plan& p, bool bf16) {
+  auto side = [&](int32_t x, bool big) { return (big && x % 256 == 0) ? 256 : 128; };
+  auto rounds_time = [&](const std::map<std::pair<int, int>, int64_t>& n) {
+    double t = 0.0;
+    for (const auto& kv : n) {
+      const int bm = kv.first.first, bn = kv.first.second;
+      if (bm == 128 && bn == 128) t += std::ceil(kv.second / (2.0 * kCUs)) * 2.0 / kSmallTileEff;
+      else t += std::ceil(kv.second / double(kCUs)) * (bm * bn / 16384.0);
+    }
+    return t;
+  };
+  for (int kind = 0; kind < 2; ++kind) {   // 0: symmetric products, 1: combine
+    bool big = false;
+    if (bf16) {
+      std::map<std::pair<int, int>, int64_t> nb, ns;
+      for (uint16_t i : p.gen) {
+        const MatDesc& d = p.desc[i];
+        const int bm = side(d.KP, true), bn = kind == 0 ? bm : side(d.NP, true);
+        const int64_t rb = d.KP / bm, cb = (kind == 0 ? d.KP : d.NP) / bn;
+        nb[{bm, bn}] += kind == 0 ? rb * (rb + 1) / 2 : rb * cb;
+        const int64_t rs = d.KP / 128, cs = (kind == 0 ? d.KP : d.NP) / 128;
+        ns[{128, 128}] += kind == 0 ? rs * (rs + 1) / 2 : rs * cs;
+      }
+      big = rounds_time(nb) < rounds_time(ns);
+    }
+    auto& lists = kind == 0 ? p.syrk : p.comb;
+    std::map<std::pair<int, int>, size_t> at;
+    for (uint16_t i : p.gen) {
+      MatDesc& d = p.desc[i];
+      const int bm = side(d.KP, big), bn = kind == 0 ? bm : side(d.NP, big);
+      auto it = at.find({bm, bn});
+      if (it == at.end()) {
+        it = at.emplace(std::make_pair(bm, bn), lists.size()).first;
+        lists.push_back({bm, bn, {}, 0});
+      }
+      if (kind == 0) {
+        add_tiles(lists[it->second].tiles, i, d.KP / bm, d.KP / bm, true);
+      } else {
+        add_tiles(lists[it->second].tiles, i, d.KP / bm, d.NP / bn, false);
+        d.n_pz = (d.KP / bm) * (d.NP / bn);
+      }
+    }
+  }
+}
+
 // Builds the plan.  `with_table` also serialises the uploaded prefix.
 muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_config_t* cfg, bool with_table,
                          Plan& p) {
@@ -205,22 +271,20 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
       d.ncb = static_cast<int32_t>(ceil_div(d.n, 512));
       d.nrb = static_cast<int32_t>(ceil_div(d.m, 32));
       d.n_pn = (d.KP / 64) * (d.NP / 64);
-      d.n_pz = (d.KP / kPad) * (d.NP / kPad);
       p.gen.push_back(static_cast<uint16_t>(i));
       for (int rb = 0; rb < d.nrb; ++rb)
         for (int cb = 0; cb < d.ncb; ++cb) p.k1.push_back({static_cast<uint16_t>(i), (uint16_t)rb, (uint16_t)cb, 0});
       for (int ti = 0; ti < d.KP / 64; ++ti)
         for (int tj = 0; tj < d.NP / 64; ++tj) p.k3.push_back({static_cast<uint16_t>(i), (uint16_t)ti, (uint16_t)tj, 0});
-      for (int ti = 0; ti < d.KP / kPad; ++ti)
-        for (int tj = ti; tj < d.KP / kPad; ++tj) p.syrk.push_back({static_cast<uint16_t>(i), (uint16_t)ti, (uint16_t)tj, 0});
-      for (int ti = 0; ti < d.KP / kPad; ++ti)
-        for (int tj = 0; tj < d.NP / kPad; ++tj) p.comb.push_back({static_cast<uint16_t>(i), (uint16_t)ti, (uint16_t)tj, 0});
       for (int ti = 0; ti < ceil_div(d.m, 64); ++ti)
         for (int tj = 0; tj < ceil_div(d.n, 64); ++tj) p.k5.push_back({static_cast<uint16_t>(i), (uint16_t)ti, (uint16_t)tj, 0});
+      d.ncond = static_cast<int32_t>(ceil_div(round_up(d.m, kPad) + round_up(d.n, kPad), 256));
+      for (int c = 0; c < d.ncond; ++c) p.cond.push_back({static_cast<uint16_t>(i), static_cast<uint16_t>(c), 0, 0});
     }
   }
   for (auto& kv : thin_groups) p.thin.push_back({kv.first, kv.second, 0});
   if (count > 65535) return fail(MUON_ERR_UNSUPPORTED, "too many matrices");
+  plan_gemm_tiles(p, cfg->ns_dtype == MUON_BF16);
 
   // Table prefix: descriptors, scalars, tile lists, id lists.
   size_t off = kAlign;   // first 256 bytes reserved
@@ -233,9 +297,10 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
   p.scal_off = take(sizeof(MatScal) * count);
   p.k1_off = take(sizeof(Tile) * p.k1.size());
   p.k3_off = take(sizeof(Tile) * p.k3.size());
-  p.syrk_off = take(sizeof(Tile) * p.syrk.size());
-  p.comb_off = take(sizeof(Tile) * p.comb.size());
+  for (auto& l : p.syrk) l.off = take(sizeof(Tile) * l.tiles.size());
+  for (auto& l : p.comb) l.off = take(sizeof(Tile) * l.tiles.size());
   p.k5_off = take(sizeof(Tile) * p.k5.size());
+  p.cond_off = take(sizeof(Tile) * p.cond.size());
   p.gen_off = take(sizeof(uint16_t) * p.gen.size());
   for (auto& g : p.thin) g.off = take(sizeof(Tile) * g.tiles.size());
   p.table_bytes = off;
@@ -262,8 +327,9 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
     d.b_off = take(static_cast<size_t>(d.KP) * d.KP * es);
     d.z_off = take(kn * 4);
     if (cfg->nesterov) d.v_off = take(static_cast<size_t>(d.m) * d.n * 4);
-    d.dr_off = take(static_cast<size_t>(d.m) * 4);
-    d.dc_off = take(static_cast<size_t>(d.n) * 4);
+    d.dr_off = take(static_cast<size_t>(round_up(d.m, kPad)) * 4);
+    d.dc_off = take(static_cast<size_t>(round_up(d.n, kPad)) * 4);
+    d.cm_off = take(static_cast<size_t>(d.ncond) * 8);
     d.pr_off = take(static_cast<size_t>(d.ncb) * d.m * 4);
     d.pc_off = take(static_cast<size_t>(d.nrb) * d.n * 4);
     d.pn_off = take(static_cast<size_t>(d.n_pn) * 4);
@@ -276,9 +342,10 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
     std::memcpy(p.table.data() + p.desc_off, p.desc.data(), sizeof(MatDesc) * count);
     put(p.table, p.k1_off, p.k1);
     put(p.table, p.k3_off, p.k3);
-    put(p.table, p.syrk_off, p.syrk);
-    put(p.table, p.comb_off, p.comb);
+    for (auto& l : p.syrk) put(p.table, l.off, l.tiles);
+    for (auto& l : p.comb) put(p.table, l.off, l.tiles);
     put(p.table, p.k5_off, p.k5);
+    put(p.table, p.cond_off, p.cond);
     put(p.table, p.gen_off, p.gen);
     for (auto& g : p.thin) put(p.table, g.off, g.tiles);
   }
@@ -441,19 +508,28 @@ muon_status_t launch_all(const Plan& p, const StepArgs& a, const Coeffs* cf, int
   if (!p.gen.empty()) {
     const int ng = static_cast<int>(p.gen.size());
     MUON_LAUNCH(MUON_LAUNCH_MOMENTUM, launch_momentum(a, tl(p.k1_off), static_cast<int>(p.k1.size()), dimuon, s));
-    if (dimuon) MUON_LAUNCH(MUON_LAUNCH_CONDITION, launch_condition(a, il(p.gen_off), ng, s));
+    if (dimuon) {
+      const int nc = static_cast<int>(p.cond.size());
+      MUON_LAUNCH(MUON_LAUNCH_CONDITION, launch_cond_energy(a, tl(p.cond_off), nc, s));
+      MUON_LAUNCH(MUON_LAUNCH_CONDITION, launch_cond_factor(a, tl(p.cond_off), nc, s));
+    }
     MUON_LAUNCH(MUON_LAUNCH_PRESCALE, launch_prescale(a, tl(p.k3_off), static_cast<int>(p.k3.size()), s));
     MUON_LAUNCH(MUON_LAUNCH_NORM, launch_norm_finalize(a, il(p.gen_off), ng, s));
-    const int nsyrk = static_cast<int>(p.syrk.size()), ncomb = static_cast<int>(p.comb.size());
+    auto nt = [](const Plan::GemmList& l) { return static_cast<int>(l.tiles.size()); };
     if (ns_steps == 0)
-      MUON_LAUNCH(MUON_LAUNCH_COMBINE,
-                  launch_combine(a, tl(p.comb_off), ncomb, 0, 1, true, true, false, Coeffs{1.0f, 0.0f, 0.0f}, s));
+      for (const auto& l : p.comb)
+        MUON_LAUNCH(MUON_LAUNCH_COMBINE, launch_combine(a, tl(l.off), nt(l), l.bm, l.bn, 0, 1, true, true, false,
+                                                        Coeffs{1.0f, 0.0f, 0.0f}, s));
     for (int t = 0; t < ns_steps; ++t) {
       const int src = t & 1, dst = src ^ 1;
       const bool first = t == 0, last = t == ns_steps - 1;
-      MUON_LAUNCH(MUON_LAUNCH_GRAM, launch_syrk(a, tl(p.syrk_off), nsyrk, 0, src, first, cf[t], s));
-      MUON_LAUNCH(MUON_LAUNCH_POLY, launch_syrk(a, tl(p.syrk_off), nsyrk, 1, src, first, cf[t], s));
-      MUON_LAUNCH(MUON_LAUNCH_COMBINE, launch_combine(a, tl(p.comb_off), ncomb, src, dst, first, last, true, cf[t], s));
+      for (const auto& l : p.syrk)
+        MUON_LAUNCH(MUON_LAUNCH_GRAM, launch_syrk(a, tl(l.off), nt(l), l.bm, 0, src, first, cf[t], s));
+      for (const auto& l : p.syrk)
+        MUON_LAUNCH(MUON_LAUNCH_POLY, launch_syrk(a, tl(l.off), nt(l), l.bm, 1, src, first, cf[t], s));
+      for (const auto& l : p.comb)
+        MUON_LAUNCH(MUON_LAUNCH_COMBINE,
+                    launch_combine(a, tl(l.off), nt(l), l.bm, l.bn, src, dst, first, last, true, cf[t], s));
     }
     if (dimuon) MUON_LAUNCH(MUON_LAUNCH_POSTNORM, launch_post_finalize(a, il(p.gen_off), ng, s));
     MUON_LAUNCH(MUON_LAUNCH_UPDATE, launch_update(a, tl(p.k5_off), static_cast<int>(p.k5.size()), s));

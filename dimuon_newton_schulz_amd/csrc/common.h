@@ -43,8 +43,10 @@ struct alignas(16) MatDesc {
   int64_t b_off;          // B = bA + c A A, KP x KP, ns dtype
   int64_t z_off;          // Z (last iterate), KP x NP, f32
   int64_t v_off;          // Nesterov input, m x n f32 (or -1)
-  int64_t dr_off;         // row factors, m f32
-  int64_t dc_off;         // column factors, n f32
+  int64_t dr_off;         // row factors, round_up(m, kPad) f32 (zero beyond m)
+  int64_t dc_off;         // column factors, round_up(n, kPad) f32 (zero beyond n)
+  int64_t cm_off;         // conditioning chunk maxima [ncond][2] f32 (rows, columns)
+  int32_t ncond;          // conditioning chunks of 256 over the padded rows, then columns
   int64_t pr_off;         // row-energy partials [ncb][m] f32
   int64_t pc_off;         // column-energy partials [nrb][n] f32
   int64_t pn_off;         // ||Y||^2 partials, one per prescale tile, f32
@@ -316,28 +318,23 @@ __device__ __forceinline__ float cond_factor(float e, float emax, float eps) {
 // --------------------------------------------------------------------------
 // Host-side launchers (defined in the .hip files)
 // --------------------------------------------------------------------------
-struct LaunchLists {
-  const Tile* k1;      int n_k1;     // momentum + energy partials tiles (general path)
-  const Tile* k3;      int n_k3;     // prescale tiles
-  const Tile* syrk;    int n_syrk;   // upper-triangular Gram tiles
-  const Tile* comb;    int n_comb;   // combine tiles
-  const Tile* k5;      int n_k5;     // final update tiles
-  const uint16_t* gen; int n_gen;    // general-path matrix ids
-  const uint16_t* thin; int n_thin;  // thin-path matrix ids (grouped by padded k)
-};
-
 hipError_t launch_momentum(const StepArgs& a, const Tile* tiles, int n, bool energies, hipStream_t s);
-hipError_t launch_condition(const StepArgs& a, const uint16_t* mats, int n, hipStream_t s);
+// Dimuon conditioning over chunks of 256 rows / columns (tiles: matrix,
+// chunk): energies and chunk maxima, then the factors (zero in the padding).
+hipError_t launch_cond_energy(const StepArgs& a, const Tile* tiles, int n, hipStream_t s);
+hipError_t launch_cond_factor(const StepArgs& a, const Tile* tiles, int n, hipStream_t s);
 hipError_t launch_prescale(const StepArgs& a, const Tile* tiles, int n, hipStream_t s);
 hipError_t launch_norm_finalize(const StepArgs& a, const uint16_t* mats, int n, hipStream_t s);
 hipError_t launch_post_finalize(const StepArgs& a, const uint16_t* mats, int n, hipStream_t s);
 hipError_t launch_update(const StepArgs& a, const Tile* tiles, int n, hipStream_t s);
-// Gram / polynomial (kind 0: A = alpha X X^T, kind 1: B = c A A + b A) and combine.
-hipError_t launch_syrk(const StepArgs& a, const Tile* tiles, int n, int kind, int src_x,
+// Gram / polynomial (kind 0: A = alpha X X^T, kind 1: B = c A A + b A) over
+// bt x bt tiles, and combine over bm x bn tiles (sides 128 or 256 for bf16
+// products; 128 for fp32).
+hipError_t launch_syrk(const StepArgs& a, const Tile* tiles, int n, int bt, int kind, int src_x,
                        bool first, Coeffs cf, hipStream_t s);
 // Combine X' = alpha (a X + B X); src/dst select the ping (0) or pong (1)
 // buffers; `product` false skips B X (used when ns_steps is 0).
-hipError_t launch_combine(const StepArgs& a, const Tile* tiles, int n, int src_x, int dst_x,
+hipError_t launch_combine(const StepArgs& a, const Tile* tiles, int n, int bm, int bn, int src_x, int dst_x,
                           bool first, bool last, bool product, Coeffs cf, hipStream_t s);
 // Thin path, one launch per phase over all slices of one padded Gram side KP:
 // energies of M_{t-1} (only when no cached energies exist), pass A

@@ -9,11 +9,25 @@
 // The symmetric products compute the upper-triangular tiles only and store
 // each such tile and its mirror.  The combine stores X' and X'^T.
 //
-// bf16 path: a 128 x 128 x 64 workgroup tile, 4 wave64 in a 2 x 2 grid, each
-// wave owning 64 x 64 as 2 x 2 v_mfma_f32_32x32x16_bf16 blocks.  LDS is
-// double-buffered and global loads for k-tile t+1 are in flight while k-tile
-// t is multiplied.  The epilogue stages the fp32 tile through LDS so that
-// both the tile and its transpose are written with 16-byte stores.
+// bf16 path: a BM x BN workgroup tile (BM, BN in {128, 256}), four wave64 in
+// a 2 x 2 grid, each wave owning (BM/2) x (BN/2) as 32 x 32 blocks of
+// v_mfma_f32_32x32x16_bf16.  Operands go from global memory straight into a
+// ring of four LDS stages of 32 k-values (global_load_lds_dwordx4, no
+// register staging), so three stages are in flight while one is multiplied
+// (the loop is pipelined so that LDS fragment reads are covered by MFMAs):
+// a 256 x 256 tile keeps 96 KB of loads outstanding per CU, enough to cover
+// the latency of L2 and HBM under a full chip of GEMM traffic.  A 256 x 256
+// tile reads half as many LDS bytes per MFMA as a 128 x 128 one and needs half
+// the L2 traffic per flop; with 128 KB of LDS and 256 accumulator registers
+// one workgroup runs per CU (two for 128 x 128).
+//
+// Epilogue without LDS: lane l of a 32 x 32 block holds, for each group of
+// four accumulators, rows i..i+3 of column j = l mod 32.  Those are
+// contiguous in the transposed output, which is written directly; for the
+// row-major output, the four lanes of a quad (four consecutive columns)
+// exchange values with DPP so that each holds one row's four columns.
+#include <type_traits>
+
 #include "common.h"
 
 namespace muon {
@@ -21,16 +35,21 @@ namespace muon {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;
-constexpr int EP_LD = BN + 1;
+constexpr int LBK = 32;   // k per pipeline stage
+constexpr int NSTG = 4;   // LDS stages: three in flight while one is multiplied
 
-struct SmemMain {
-  uint16_t a[2][BM][LDK];
-  uint16_t b[2][BN][LDK];
+template <int BM, int BN>
+struct GemmT {
+  static constexpr int MS = BM / 64, NS = BN / 64;   // 32 x 32 blocks per wave
+  static constexpr int LA = BM / 64, LB = BN / 64;   // 16-byte LDS loads per thread and stage
+  static constexpr int LPS = LA + LB;
+  static constexpr int STAGE = (BM + BN) * LBK;      // bf16 elements per stage: A rows, then B rows
+  static constexpr int SP = BM / 2 + 2;              // epilogue staging row stride (floats)
+  union Smem {
+    uint16_t buf[NSTG][STAGE];
+    float st[BN * SP];                               // half a tile, transposed, fp32
+  };
 };
-constexpr int kSmemMain = sizeof(SmemMain);
-constexpr int kSmemEpi = BM * EP_LD * 4;
-constexpr int kSmemBytes = kSmemMain > kSmemEpi ? kSmemMain : kSmemEpi;
 
 // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous
 // run of the tile list so that tiles sharing operand panels share an L2.
@@ -40,126 +59,250 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
 }
 
-// acc[s][t] += P[rows wr*64+s*32..][k] * Q[rows wc*64+t*32..][k] over k < K.
-__device__ __forceinline__ void mma_nt_bf16(const uint16_t* __restrict__ Pg, int64_t ldp,
-                                            const uint16_t* __restrict__ Qg, int64_t ldq, int K,
-                                            SmemMain& sm, f32x16_t acc[2][2]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// s_waitcnt with only the vector-memory counter limited to N (N <= 63).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// A stage holds rows of 32 k-values (64 bytes, four 16-byte chunks).  Chunk
+// c of row r sits at chunk slot c ^ ((r >> 2) & 3): the 32 rows a fragment
+// read touches at one logical chunk then spread over all banks.
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+
+// Direct global -> LDS loads of stage `st` (k0 = st * LBK) into buffer b.  A
+// wave's load writes 64 consecutive 16-byte LDS chunks (16 rows); each lane
+// fetches the global chunk that belongs in its slot.
+template <int BM, int BN>
+__device__ __forceinline__ void issue_stage(const MUON_GLOBAL uint16_t* P, int64_t ldp, const MUON_GLOBAL uint16_t* Q,
+                                            int64_t ldq, int st, uint16_t* buf) {
+  using G = GemmT<BM, BN>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int k0 = st * LBK;
+#pragma unroll
+  for (int q = 0; q < G::LA + G::LB; ++q) {
+    const bool is_a = q < G::LA;
+    const int blk = (is_a ? q : q - G::LA) * 4 + wave;
+    const int row = blk * 16 + (lane >> 2);
+    const int lch = (lane & 3) ^ swz(row);
+    const MUON_GLOBAL uint16_t* src = is_a ? P + row * ldp + k0 + lch * 8 : Q + row * ldq + k0 + lch * 8;
+    uint16_t* dst = buf + (is_a ? 0 : BM * LBK) + blk * 512;
+    __builtin_amdgcn_global_load_lds((const MUON_GLOBAL void*)(src), (__attribute__((address_space(3))) void*)(dst),
+                                     16, 0, 0);
+  }
+}
+
+// acc[s][t] += P[rows wr*BM/2 + s*32 ..][k] * Q[rows wc*BN/2 + t*32 ..][k] over k < K
+// (K a multiple of 4 * LBK).  A stage holds two k-halves of 16.  Iteration kt:
+//   read half 1 of stage kt;  MFMAs of half 0 (read in the previous iteration)
+//   wait for this wave's loads of stage kt+1; barrier
+//   load stage kt+4 into stage kt's buffer (every wave has its fragments of
+//   stage kt in registers: LDS reads complete before the barrier)
+//   read half 0 of stage kt+1;  MFMAs of half 1
+// so fragment reads are always covered by MFMAs, and three stages are in
+// flight while one is multiplied.  The first four stages are issued before
+// the loop.
+template <int BM, int BN>
+__device__ __forceinline__ void mma_nt_bf16(const uint16_t* Pg, int64_t ldp, const uint16_t* Qg, int64_t ldq,
+                                            int K, typename GemmT<BM, BN>::Smem& sm,
+                                            f32x16_t (&acc)[BM / 64][BN / 64]) {
+  using G = GemmT<BM, BN>;
+  constexpr int MS = G::MS, NS = G::NS, LPS = G::LPS;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = wave >> 1, wc = wave & 1;
-  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-  // Chunk q of this thread: row (tid + 256 q) / 8, 16-byte column (tid & 7).
-  const int crow = tid >> 3, ccol = (tid & 7) * 8;
-  const uint16_t* pa = Pg + crow * ldp + ccol;
-  const uint16_t* pb = Qg + crow * ldq + ccol;
-  const int64_t sa = 32 * ldp, sb = 32 * ldq;   // 256 chunks = 32 rows further
-#define MUON_GLOAD(k0)                                                        \
-  ra0 = *reinterpret_cast<const uint4*>(pa + (k0));                           \
-  ra1 = *reinterpret_cast<const uint4*>(pa + sa + (k0));                      \
-  ra2 = *reinterpret_cast<const uint4*>(pa + 2 * sa + (k0));                  \
-  ra3 = *reinterpret_cast<const uint4*>(pa + 3 * sa + (k0));                  \
-  rb0 = *reinterpret_cast<const uint4*>(pb + (k0));                           \
-  rb1 = *reinterpret_cast<const uint4*>(pb + sb + (k0));                      \
-  rb2 = *reinterpret_cast<const uint4*>(pb + 2 * sb + (k0));                  \
-  rb3 = *reinterpret_cast<const uint4*>(pb + 3 * sb + (k0));
-#define MUON_SSTORE(buf)                                                      \
-  *reinterpret_cast<uint4*>(&sm.a[buf][crow][ccol]) = ra0;                    \
-  *reinterpret_cast<uint4*>(&sm.a[buf][crow + 32][ccol]) = ra1;               \
-  *reinterpret_cast<uint4*>(&sm.a[buf][crow + 64][ccol]) = ra2;               \
-  *reinterpret_cast<uint4*>(&sm.a[buf][crow + 96][ccol]) = ra3;               \
-  *reinterpret_cast<uint4*>(&sm.b[buf][crow][ccol]) = rb0;                    \
-  *reinterpret_cast<uint4*>(&sm.b[buf][crow + 32][ccol]) = rb1;               \
-  *reinterpret_cast<uint4*>(&sm.b[buf][crow + 64][ccol]) = rb2;               \
-  *reinterpret_cast<uint4*>(&sm.b[buf][crow + 96][ccol]) = rb3;
-  MUON_GLOAD(0)
-  MUON_SSTORE(0)
-  __syncthreads();
-  const int nk = K / BK;
-  const int fr = lane & 31, fk = 8 * (lane >> 5);
+  const MUON_GLOBAL uint16_t* P = gmem(Pg);
+  const MUON_GLOBAL uint16_t* Q = gmem(Qg);
+  const int nk = K / LBK;
+#pragma unroll
+  for (int st = 0; st < NSTG; ++st)
+    if (st < nk) issue_stage<BM, BN>(P, ldp, Q, ldq, st, sm.buf[st]);
+  // Fragment addresses (elements within a stage): row (lane & 31) of each
+  // 32-row block, logical chunk 2 kk + (lane >> 5).
+  const int fr = lane & 31, sw = swz(fr);
+  const int ch0 = ((lane >> 5) ^ sw) * 8, ch1 = ((2 + (lane >> 5)) ^ sw) * 8;
+  const int a_off = (wr * (BM / 2) + fr) * LBK, b_off = BM * LBK + (wc * (BN / 2) + fr) * LBK;
+  bf16x8_t fa0[MS], fb0[NS], fa1[MS], fb1[NS];
+  auto read_half = [&](const uint16_t* buf, int ch, bf16x8_t (&fa)[MS], bf16x8_t (&fb)[NS]) {
+#pragma unroll
+    for (int s = 0; s < MS; ++s) fa[s] = *reinterpret_cast<const bf16x8_t*>(buf + a_off + s * 32 * LBK + ch);
+#pragma unroll
+    for (int t = 0; t < NS; ++t) fb[t] = *reinterpret_cast<const bf16x8_t*>(buf + b_off + t * 32 * LBK + ch);
+  };
+  auto mfma_half = [&](const bf16x8_t (&fa)[MS], const bf16x8_t (&fb)[NS]) {
+#pragma unroll
+    for (int s = 0; s < MS; ++s)
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+        acc[s][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s], fb[t], acc[s][t], 0, 0, 0);
+  };
+  // Stage 0 landed (loads issued after it: stages 1 .. 3, if any).
+  if (nk >= 4) wait_vm<3 * LPS>();
+  else if (nk == 3) wait_vm<2 * LPS>();
+  else if (nk == 2) wait_vm<LPS>();
+  else wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  read_half(sm.buf[0], ch0, fa0, fb0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) { MUON_GLOAD((kt + 1) * BK) }
+    const uint16_t* buf = sm.buf[kt % NSTG];
+    read_half(buf, ch1, fa1, fb1);
+    mfma_half(fa0, fb0);
+    // (The scheduling barriers keep the MFMAs on their side of the wait.)
+    __builtin_amdgcn_sched_barrier(0);
+    // This wave's reads of stage kt are complete; stage kt+1 has landed.
+    const int left = nk - 2 - kt;   // stages issued after kt+1
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    if (left >= 2) wait_vm<2 * LPS>();
+    else if (left == 1) wait_vm<LPS>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + NSTG < nk) issue_stage<BM, BN>(P, ldp, Q, ldq, kt + NSTG, sm.buf[kt % NSTG]);
+    if (kt + 1 < nk) read_half(sm.buf[(kt + 1) % NSTG], ch0, fa0, fb0);
+    mfma_half(fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Calls f(integral_constant<int, I>) for I = I0 .. N-1: compile-time block
+// indices, so that the accumulators are never indexed at run time.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Tile-relative column of block t for this lane (rows of a block's
+// accumulator group g are 8g + 4 (lane >> 5) + 0..3).
+template <int BN>
+__device__ __forceinline__ int blk_col(int t) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  return (wave & 1) * (BN / 2) + t * 32 + (lane & 31);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+// Eight consecutive values at element idx: bf16 (16 bytes) or f32 (32 bytes).
+__device__ __forceinline__ void store8(void* p, int64_t idx, int32_t dt, const float (&v)[8]) {
+  if (dt == DT_BF16) {
+    *reinterpret_cast<MUON_GLOBAL uint4*>(gmem(static_cast<uint16_t*>(p)) + idx) =
+        make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                   pack_bf16x2(v[6], v[7]));
+  } else {
+    MUON_GLOBAL float4* q = reinterpret_cast<MUON_GLOBAL float4*>(gmem(static_cast<float*>(p)) + idx);
+    q[0] = make_float4(v[0], v[1], v[2], v[3]);
+    q[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+__device__ __forceinline__ uint4 fetch8_bf16(const uint16_t* p, int64_t idx) {
+  return *reinterpret_cast<const MUON_GLOBAL uint4*>(gmem(p) + idx);
+}
+
+__device__ __forceinline__ void unpack8_bf16(const uint4& u, float (&v)[8]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t fa[2], fb[2];
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = __uint_as_float(w[e] << 16);
+    v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+  }
+}
+
+// Epilogue through LDS, in two rounds.  In round r every wave stages its
+// accumulator blocks s in [r MS/2, (r+1) MS/2), as fp32 and transposed:
+// st[j][il], where staged row il stands for tile row
+//   i(il) = (il / Q) * BM/2 + r * Q + il % Q,   Q = BM/4
+// (the round's quarter of each wave row).  From each round, every thread
+// produces whole 8-element chunks:
+//   out_t(j, i0, v, aux): v[e] = acc of tile element (i0 + e, j)  (a column
+//                         run; contiguous in the transposed output)
+//   out_n(i, j0, v, aux): v[e] = acc of tile element (i, j0 + e)  (a row run)
+// so that all global reads and writes are 16-byte runs.  aux_t(j, i0) and
+// aux_n(i, j0) fetch 8 bf16 operand values per chunk (or nothing); a thread
+// issues all of a round's column-run fetches before staging and all of its
+// row-run fetches right after, so that they are in flight together.  The row
+// stride SP = BM/2 + 2 keeps both the column-run reads (consecutive lanes
+// along il) and the row-run reads (16 lanes along il x 4 along j) free of
+// bank conflicts.
+template <int BM, int BN, typename AT, typename AN, typename FT, typename FN>
+__device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[BM / 64][BN / 64],
+                                                typename GemmT<BM, BN>::Smem& sm, bool do_t, bool do_n,
+                                                AT&& aux_t, AN&& aux_n, FT&& out_t, FN&& out_n) {
+  using G = GemmT<BM, BN>;
+  constexpr int SP = G::SP, HM = BM / 2, QM = BM / 4, MH = G::MS / 2;
+  constexpr int CPR = HM / 8;                 // column-run chunks per staged row
+  constexpr int CT = BN * CPR / 256;          // column-run chunks per thread and round
+  constexpr int NB = HM / 16;                 // blocks of 16 staged rows (row runs)
+  constexpr int CN = HM * (BN / 8) / 256;     // row-run chunks per thread and round
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wr = wave >> 1;
+  float* st = sm.st;
+  auto t_pos = [&](int q, int& j, int& il) {
+    const int c = tid + 256 * q;
+    j = c / CPR;
+    il = (c % CPR) * 8;
+  };
+  auto n_pos = [&](int q, int& il, int& j0) {
+    const int c = tid + 256 * q;
+    const int i16 = c & 15, jl = (c >> 4) & 3, r = c >> 6;
+    il = (r % NB) * 16 + i16;
+    j0 = ((r / NB) * 4 + jl) * 8;
+  };
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        fa[s] = *reinterpret_cast<const bf16x8_t*>(&sm.a[cur][wr * 64 + s * 32 + fr][kk * 16 + fk]);
-        fb[s] = *reinterpret_cast<const bf16x8_t*>(&sm.b[cur][wc * 64 + s * 32 + fr][kk * 16 + fk]);
-      }
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          acc[s][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s], fb[t], acc[s][t], 0, 0, 0);
-    }
-    if (kt + 1 < nk) { MUON_SSTORE(cur ^ 1) }
+  for (int rd = 0; rd < 2; ++rd) {
+    auto row_of = [&](int il) { return (il / QM) * HM + rd * QM + il % QM; };
+    uint4 xt[CT], xn[CN];
+    if (do_t)
+      static_for<0, CT>([&](auto q) {
+        int j, il;
+        t_pos(q, j, il);
+        xt[q] = aux_t(j, row_of(il));
+      });
+    __syncthreads();   // the main loop's stages, or the previous round, are no longer read
+    static_for<0, MH * G::NS * 4>([&](auto q) {
+      constexpr int sl = q / (G::NS * 4), u = (q / 4) % G::NS, g = q % 4;
+      const int s = rd * MH + sl;
+      const int il = wr * QM + sl * 32 + 8 * g + 4 * (lane >> 5);
+      float* p = st + blk_col<BN>(u) * SP + il;
+      *reinterpret_cast<float2*>(p) = make_float2(acc[s][u][4 * g], acc[s][u][4 * g + 1]);
+      *reinterpret_cast<float2*>(p + 2) = make_float2(acc[s][u][4 * g + 2], acc[s][u][4 * g + 3]);
+    });
     __syncthreads();
-  }
-#undef MUON_GLOAD
-#undef MUON_SSTORE
-}
-
-// Position of accumulator element r of block (s, t) inside the 128 x 128 tile.
-__device__ __forceinline__ int acc_row(int s, int r) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  return (wave >> 1) * 64 + s * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-}
-__device__ __forceinline__ int acc_col(int t) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  return (wave & 1) * 64 + t * 32 + (lane & 31);
-}
-
-// Store the staged fp32 tile ep[BM][EP_LD] at dst (row0, col0), and / or its
-// transpose at dstT (col0, row0).  dt selects bf16 or f32 storage.
-__device__ __forceinline__ void store_tile(const float* ep, void* dst, int64_t ld, int64_t row0,
-                                           int64_t col0, int32_t dt) {
-  const int tid = threadIdx.x, r = tid >> 1, c0 = (tid & 1) * 64;
-  const float* src = ep + r * EP_LD + c0;
-  if (dt == DT_BF16) {
-    uint4* q = reinterpret_cast<uint4*>(static_cast<uint16_t*>(dst) + (row0 + r) * ld + col0 + c0);
+    // Row-run operands are fetched now and arrive while the column runs are
+    // written.
+    if (do_n)
+      static_for<0, CN>([&](auto q) {
+        int il, j0;
+        n_pos(q, il, j0);
+        xn[q] = aux_n(row_of(il), j0);
+      });
+    if (do_t)
+      static_for<0, CT>([&](auto q) {
+        int j, il;
+        t_pos(q, j, il);
+        const float* p = st + j * SP + il;
+        float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint4 u;
-      u.x = f32_to_bf16(src[8 * e + 0]) | (static_cast<uint32_t>(f32_to_bf16(src[8 * e + 1])) << 16);
-      u.y = f32_to_bf16(src[8 * e + 2]) | (static_cast<uint32_t>(f32_to_bf16(src[8 * e + 3])) << 16);
-      u.z = f32_to_bf16(src[8 * e + 4]) | (static_cast<uint32_t>(f32_to_bf16(src[8 * e + 5])) << 16);
-      u.w = f32_to_bf16(src[8 * e + 6]) | (static_cast<uint32_t>(f32_to_bf16(src[8 * e + 7])) << 16);
-      q[e] = u;
-    }
-  } else {
-    float4* q = reinterpret_cast<float4*>(static_cast<float*>(dst) + (row0 + r) * ld + col0 + c0);
+        for (int e = 0; e < 8; e += 2) {
+          const float2 w = *reinterpret_cast<const float2*>(p + e);
+          v[e] = w.x;
+          v[e + 1] = w.y;
+        }
+        out_t(j, row_of(il), v, xt[q]);
+      });
+    if (do_n)
+      static_for<0, CN>([&](auto q) {
+        int il, j0;
+        n_pos(q, il, j0);
+        float v[8];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) q[e] = make_float4(src[4 * e], src[4 * e + 1], src[4 * e + 2], src[4 * e + 3]);
-  }
-}
-
-__device__ __forceinline__ void store_tile_t(const float* ep, void* dst, int64_t ld, int64_t row0,
-                                             int64_t col0, int32_t dt) {
-  // dst[(col0 + j) * ld + row0 + i] = ep[i][j]
-  const int tid = threadIdx.x, j = tid >> 1, i0 = (tid & 1) * 64;
-  if (dt == DT_BF16) {
-    uint4* q = reinterpret_cast<uint4*>(static_cast<uint16_t*>(dst) + (col0 + j) * ld + row0 + i0);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v[8];
-#pragma unroll
-      for (int h = 0; h < 8; ++h) v[h] = ep[(i0 + 8 * e + h) * EP_LD + j];
-      uint4 u;
-      u.x = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-      u.y = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-      u.z = f32_to_bf16(v[4]) | (static_cast<uint32_t>(f32_to_bf16(v[5])) << 16);
-      u.w = f32_to_bf16(v[6]) | (static_cast<uint32_t>(f32_to_bf16(v[7])) << 16);
-      q[e] = u;
-    }
-  } else {
-    float4* q = reinterpret_cast<float4*>(static_cast<float*>(dst) + (col0 + j) * ld + row0 + i0);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float v[4];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) v[h] = ep[(i0 + 4 * e + h) * EP_LD + j];
-      q[e] = make_float4(v[0], v[1], v[2], v[3]);
-    }
+        for (int e = 0; e < 8; ++e) v[e] = st[(j0 + e) * SP + il];
+        out_n(row_of(il), j0, v, xn[q]);
+      });
   }
 }
 
@@ -174,12 +317,14 @@ __device__ __forceinline__ float block_sum256(float v, float* sh) {
 }
 
 // ---------------------------------------------------------------------------
-// Symmetric products (bf16): kind 0 Gram, kind 1 polynomial.
+// Symmetric products (bf16): kind 0 Gram, kind 1 polynomial.  Square tiles.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_syrk_bf16(StepArgs a, const Tile* __restrict__ tiles, int ntiles,
-                                                   int kind, int src_x, int first, Coeffs cf) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  SmemMain& sm = *reinterpret_cast<SmemMain*>(smem);
+template <int BT, int KIND>
+__global__ __launch_bounds__(256, 1) void k_syrk_bf16(StepArgs a, const Tile* __restrict__ tiles, int ntiles,
+                                                   int src_x, int first, Coeffs cf) {
+  constexpr int kind = KIND;
+  using G = GemmT<BT, BT>;
+  __shared__ typename G::Smem sm;
   const Tile t = tiles[xcd_remap(blockIdx.x, ntiles)];
   const MatDesc& d = a.desc[t.mat];
   const uint16_t* P;
@@ -191,99 +336,133 @@ __global__ __launch_bounds__(256) void k_syrk_bf16(StepArgs a, const Tile* __res
     P = reinterpret_cast<const uint16_t*>(a.ws + d.a_off);
     ld = d.KP;
   }
-  const int K = static_cast<int>(ld);
-  f32x16_t acc[2][2];
+  f32x16_t acc[G::MS][G::NS];
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int s = 0; s < G::MS; ++s)
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < G::NS; ++u)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[s][u][r] = 0.0f;
-  mma_nt_bf16(P + static_cast<int64_t>(t.ti) * BM * ld, ld, P + static_cast<int64_t>(t.tj) * BN * ld, ld, K,
-              sm, acc);
+  mma_nt_bf16<BT, BT>(P + static_cast<int64_t>(t.ti) * BT * ld, ld, P + static_cast<int64_t>(t.tj) * BT * ld, ld,
+                      static_cast<int>(ld), sm, acc);
 
   const float alpha = (kind == 0) ? (first ? a.scal[d.scal_idx].inv_nu2 : 1.0f) : cf.c;
   const uint16_t* E = reinterpret_cast<const uint16_t*>(a.ws + d.a_off);
-  float* ep = reinterpret_cast<float*>(smem);
-  const int64_t gi0 = static_cast<int64_t>(t.ti) * BM, gj0 = static_cast<int64_t>(t.tj) * BN;
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = acc_row(s, r), j = acc_col(u);
-        float v = alpha * acc[s][u][r];
-        if (kind == 1) v = v + cf.b * bf16_to_f32(E[(gi0 + i) * d.KP + gj0 + j]);
-        ep[i * EP_LD + j] = v;
-      }
-  __syncthreads();
   void* dst = a.ws + (kind == 0 ? d.a_off : d.b_off);
-  store_tile(ep, dst, d.KP, gi0, gj0, DT_BF16);
-  if (t.ti != t.tj) store_tile_t(ep, dst, d.KP, gi0, gj0, DT_BF16);
+  const int64_t gi0 = static_cast<int64_t>(t.ti) * BT, gj0 = static_cast<int64_t>(t.tj) * BT;
+  const int64_t ldo = d.KP;
+  // Element (i, j) of the tile goes to (gi0 + i, gj0 + j) and, mirrored, to
+  // (gj0 + j, gi0 + i); a diagonal tile is symmetric, so the mirrored store
+  // alone writes all of it.  E (= A) is symmetric: E[i][j] = E[j][i].
+  auto aux_t = [&](int j, int i0) {
+    return kind == 1 ? fetch8_bf16(E, (gj0 + j) * ldo + gi0 + i0) : make_uint4(0, 0, 0, 0);
+  };
+  auto aux_n = [&](int i, int j0) {
+    return kind == 1 ? fetch8_bf16(E, (gi0 + i) * ldo + gj0 + j0) : make_uint4(0, 0, 0, 0);
+  };
+  auto fin = [&](float (&v)[8], const uint4& aux) {
+    float e8[8];
+    unpack8_bf16(aux, e8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = kind == 1 ? alpha * v[e] + cf.b * e8[e] : alpha * v[e];
+  };
+  auto out_t = [&](int j, int i0, float (&v)[8], const uint4& aux) {
+    fin(v, aux);
+    store8(dst, (gj0 + j) * ldo + gi0 + i0, DT_BF16, v);
+  };
+  auto out_n = [&](int i, int j0, float (&v)[8], const uint4& aux) {
+    fin(v, aux);
+    store8(dst, (gi0 + i) * ldo + gj0 + j0, DT_BF16, v);
+  };
+  staged_epilogue<BT, BT>(acc, sm, true, t.ti != t.tj, aux_t, aux_n, out_t, out_n);
 }
 
 // ---------------------------------------------------------------------------
 // Combine (bf16 operands): X' = alpha (a X + B X).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_combine_bf16(StepArgs a, const Tile* __restrict__ tiles, int ntiles,
-                                                      int src_x, int dst_x, int first, int last, int product,
-                                                      Coeffs cf) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  __shared__ float red[4];
-  SmemMain& sm = *reinterpret_cast<SmemMain*>(smem);
+template <int BM, int BN, bool LAST>
+__global__ __launch_bounds__(256, 1) void k_combine_bf16(StepArgs a, const Tile* __restrict__ tiles, int ntiles,
+                                                      int src_x, int dst_x, int first, int product, Coeffs cf) {
+  constexpr bool last = LAST;
+  using G = GemmT<BM, BN>;
+  __shared__ typename G::Smem sm;
   const Tile t = tiles[xcd_remap(blockIdx.x, ntiles)];
   const MatDesc& d = a.desc[t.mat];
   const uint16_t* Bm = reinterpret_cast<const uint16_t*>(a.ws + d.b_off);
-  const uint16_t* X = reinterpret_cast<const uint16_t*>(a.ws + d.x_off[2 * src_x]);
   const uint16_t* XT = reinterpret_cast<const uint16_t*>(a.ws + d.x_off[2 * src_x + 1]);
-  f32x16_t acc[2][2];
+  f32x16_t acc[G::MS][G::NS];
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int s = 0; s < G::MS; ++s)
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < G::NS; ++u)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[s][u][r] = 0.0f;
   if (product)
-    mma_nt_bf16(Bm + static_cast<int64_t>(t.ti) * BM * d.KP, d.KP, XT + static_cast<int64_t>(t.tj) * BN * d.KP,
-                d.KP, d.KP, sm, acc);
+    mma_nt_bf16<BM, BN>(Bm + static_cast<int64_t>(t.ti) * BM * d.KP, d.KP,
+                        XT + static_cast<int64_t>(t.tj) * BN * d.KP, d.KP, d.KP, sm, acc);
 
   const float alpha = first ? a.scal[d.scal_idx].inv_nu : 1.0f;
-  float* ep = reinterpret_cast<float*>(smem);
   const int64_t gi0 = static_cast<int64_t>(t.ti) * BM, gj0 = static_cast<int64_t>(t.tj) * BN;
-  const bool partials = last && a.dimuon;
-  const float* dgr = reinterpret_cast<const float*>(a.ws + (d.tall ? d.dc_off : d.dr_off));
-  const float* dgc = reinterpret_cast<const float*>(a.ws + (d.tall ? d.dr_off : d.dc_off));
+  const bool partials = LAST && a.dimuon;
+  const uint16_t* X = reinterpret_cast<const uint16_t*>(a.ws + d.x_off[2 * src_x]);
+  const MUON_GLOBAL float* dgr = gmem(reinterpret_cast<const float*>(a.ws + (d.tall ? d.dc_off : d.dr_off)));
+  const MUON_GLOBAL float* dgc = gmem(reinterpret_cast<const float*>(a.ws + (d.tall ? d.dr_off : d.dc_off)));
+  // X' (row-major, NP) and X'^T (KP) while iterating; on the last iteration Z
+  // (f32) in the caller's orientation: row-major for wide, transposed for tall.
+  void* dst_n = last ? (d.tall ? nullptr : a.ws + d.z_off) : a.ws + d.x_off[2 * dst_x];
+  void* dst_t = last ? (d.tall ? a.ws + d.z_off : nullptr) : a.ws + d.x_off[2 * dst_x + 1];
+  const int32_t odt = last ? DT_F32 : DT_BF16;
   float sz = 0.0f, sp = 0.0f;
+  // Dimuon's norm partials: sum of v^2 and of (fr v fc)^2 over the tile, with
+  // fr, fc the factors of the Gram orientation's rows and columns (the factor
+  // arrays are zero in the padding).
+  auto factors8 = [&](const MUON_GLOBAL float* f, int64_t at, float (&r)[8]) {
+    const float4 lo = *reinterpret_cast<const MUON_GLOBAL float4*>(f + at);
+    const float4 hi = *reinterpret_cast<const MUON_GLOBAL float4*>(f + at + 4);
+    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+  };
+  auto accum = [&](float fr, float v, float fc) {
+    const float p = (fr * v) * fc;
+    sz = sz + v * v;
+    sp = sp + p * p;
+  };
+  // X[i][j] = X^T[j][i]: column runs read X^T, row runs read X.
+  auto aux_t = [&](int j, int i0) { return fetch8_bf16(XT, (gj0 + j) * d.KP + gi0 + i0); };
+  auto aux_n = [&](int i, int j0) { return fetch8_bf16(X, (gi0 + i) * d.NP + gj0 + j0); };
+  auto out_t = [&](int j, int i0, float (&v)[8], const uint4& aux) {
+    float x[8];
+    unpack8_bf16(aux, x);
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+    for (int e = 0; e < 8; ++e) v[e] = alpha * (cf.a * x[e] + v[e]);
+    if (LAST && partials) {
+      float fr[8];
+      factors8(dgr, gi0 + i0, fr);
+      const float fc = dgc[gj0 + j];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+      for (int e = 0; e < 8; ++e) accum(fr[e], v[e], fc);
+    }
+    store8(dst_t, (gj0 + j) * d.KP + gi0 + i0, odt, v);
+  };
+  auto out_n = [&](int i, int j0, float (&v)[8], const uint4& aux) {
+    float x[8];
+    unpack8_bf16(aux, x);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = acc_row(s, r), j = acc_col(u);
-        const float x = bf16_to_f32(X[(gi0 + i) * d.NP + gj0 + j]);
-        const float v = alpha * (cf.a * x + acc[s][u][r]);
-        ep[i * EP_LD + j] = v;
-        if (partials) {
-          const int64_t gi = gi0 + i, gj = gj0 + j;
-          const float fr = gi < d.k ? dgr[gi] : 0.0f;
-          const float fc = gj < d.N ? dgc[gj] : 0.0f;
-          const float p = (fr * v) * fc;
-          sz = sz + v * v;
-          sp = sp + p * p;
-        }
-      }
-  __syncthreads();
-  if (!last) {
-    store_tile(ep, a.ws + d.x_off[2 * dst_x], d.NP, gi0, gj0, DT_BF16);
-    store_tile_t(ep, a.ws + d.x_off[2 * dst_x + 1], d.KP, gi0, gj0, DT_BF16);
-  } else if (d.tall) {
-    store_tile_t(ep, a.ws + d.z_off, d.KP, gi0, gj0, DT_F32);
-  } else {
-    store_tile(ep, a.ws + d.z_off, d.NP, gi0, gj0, DT_F32);
-  }
-  if (partials) {
+    for (int e = 0; e < 8; ++e) v[e] = alpha * (cf.a * x[e] + v[e]);
+    if (LAST && partials) {
+      float fc[8];
+      factors8(dgc, gj0 + j0, fc);
+      const float fr = dgr[gi0 + i];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) accum(fr, v[e], fc[e]);
+    }
+    store8(dst_n, (gi0 + i) * d.NP + gj0 + j0, odt, v);
+  };
+  staged_epilogue<BM, BN>(acc, sm, dst_t != nullptr, dst_n != nullptr, aux_t, aux_n, out_t, out_n);
+  if (LAST && partials) {
+    // The stage buffers are free once every wave has left the main loop.
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(sm.buf[0]);
     sz = block_sum256(sz, red);
     sp = block_sum256(sp, red);
     if (threadIdx.x == 0) {
@@ -299,7 +478,7 @@ __global__ __launch_bounds__(256) void k_combine_bf16(StepArgs a, const Tile* __
 // fp32 path (ns dtype F32): the same products with IEEE fp32 multiply-adds.
 // 128 x 128 tile, 256 threads, each an 8 x 8 micro-tile; K in steps of 16.
 // ---------------------------------------------------------------------------
-constexpr int FBK = 16, FLD = 128 + 4;
+constexpr int FBK = 16, FLD = 128 + 4, FT = 128;
 
 __device__ __forceinline__ void mma_nt_f32(const float* __restrict__ Pg, int64_t ldp,
                                            const float* __restrict__ Qg, int64_t ldq, int K,
@@ -344,13 +523,13 @@ __global__ __launch_bounds__(256) void k_syrk_f32(StepArgs a, const Tile* __rest
     ld = d.KP;
   }
   float acc[8][8] = {};
-  mma_nt_f32(P + static_cast<int64_t>(t.ti) * BM * ld, ld, P + static_cast<int64_t>(t.tj) * BN * ld, ld,
+  mma_nt_f32(P + static_cast<int64_t>(t.ti) * FT * ld, ld, P + static_cast<int64_t>(t.tj) * FT * ld, ld,
              static_cast<int>(ld), As, Bs, acc);
   const float alpha = (kind == 0) ? (first ? a.scal[d.scal_idx].inv_nu2 : 1.0f) : cf.c;
   const float* E = reinterpret_cast<const float*>(a.ws + d.a_off);
   float* C = reinterpret_cast<float*>(a.ws + (kind == 0 ? d.a_off : d.b_off));
   const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
-  const int64_t gi0 = static_cast<int64_t>(t.ti) * BM + ty * 8, gj0 = static_cast<int64_t>(t.tj) * BN + tx * 8;
+  const int64_t gi0 = static_cast<int64_t>(t.ti) * FT + ty * 8, gj0 = static_cast<int64_t>(t.tj) * FT + tx * 8;
   float v[8][8];
 #pragma unroll
   for (int r = 0; r < 8; ++r)
@@ -387,11 +566,11 @@ __global__ __launch_bounds__(256) void k_combine_f32(StepArgs a, const Tile* __r
   const float* XT = reinterpret_cast<const float*>(a.ws + d.x_off[2 * src_x + 1]);
   float acc[8][8] = {};
   if (product)
-    mma_nt_f32(Bm + static_cast<int64_t>(t.ti) * BM * d.KP, d.KP, XT + static_cast<int64_t>(t.tj) * BN * d.KP,
+    mma_nt_f32(Bm + static_cast<int64_t>(t.ti) * FT * d.KP, d.KP, XT + static_cast<int64_t>(t.tj) * FT * d.KP,
                d.KP, d.KP, As, Bs, acc);
   const float alpha = first ? a.scal[d.scal_idx].inv_nu : 1.0f;
   const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
-  const int64_t gi0 = static_cast<int64_t>(t.ti) * BM + ty * 8, gj0 = static_cast<int64_t>(t.tj) * BN + tx * 8;
+  const int64_t gi0 = static_cast<int64_t>(t.ti) * FT + ty * 8, gj0 = static_cast<int64_t>(t.tj) * FT + tx * 8;
   const bool partials = last && a.dimuon;
   const float* dgr = reinterpret_cast<const float*>(a.ws + (d.tall ? d.dc_off : d.dr_off));
   const float* dgc = reinterpret_cast<const float*>(a.ws + (d.tall ? d.dr_off : d.dc_off));
@@ -440,7 +619,7 @@ __global__ __launch_bounds__(256) void k_combine_f32(StepArgs a, const Tile* __r
     sp = block_sum256(sp, red);
     if (threadIdx.x == 0) {
       float* pz = reinterpret_cast<float*>(a.ws + d.pz_off);
-      const int idx = t.ti * (d.NP / BN) + t.tj;
+      const int idx = t.ti * (d.NP / FT) + t.tj;
       pz[2 * idx] = sz;
       pz[2 * idx + 1] = sp;
     }
@@ -448,27 +627,55 @@ __global__ __launch_bounds__(256) void k_combine_f32(StepArgs a, const Tile* __r
 }
 
 // ---------------------------------------------------------------------------
-// Launchers
+// Launchers.  bt / bm, bn: tile sides of the list (128 or 256; fp32 always 128).
 // ---------------------------------------------------------------------------
-hipError_t launch_syrk(const StepArgs& a, const Tile* tiles, int n, int kind, int src_x, bool first,
+hipError_t launch_syrk(const StepArgs& a, const Tile* tiles, int n, int bt, int kind, int src_x, bool first,
                        Coeffs cf, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  if (a.ns_dt == DT_BF16)
-    hipLaunchKernelGGL(k_syrk_bf16, dim3(n), dim3(256), 0, s, a, tiles, n, kind, src_x, first ? 1 : 0, cf);
-  else
-    hipLaunchKernelGGL(k_syrk_f32, dim3(n), dim3(256), 0, s, a, tiles, n, kind, src_x, first ? 1 : 0, cf);
+  const int f = first ? 1 : 0;
+  if (a.ns_dt != DT_BF16) {
+    if (bt != 128) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_syrk_f32, dim3(n), dim3(256), 0, s, a, tiles, n, kind, src_x, f, cf);
+    return hipGetLastError();
+  }
+#define MUON_SYRK(BT, K) hipLaunchKernelGGL((k_syrk_bf16<BT, K>), dim3(n), dim3(256), 0, s, a, tiles, n, src_x, f, cf)
+  if (bt == 256) {
+    if (kind == 0) MUON_SYRK(256, 0); else MUON_SYRK(256, 1);
+  } else if (bt == 128) {
+    if (kind == 0) MUON_SYRK(128, 0); else MUON_SYRK(128, 1);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef MUON_SYRK
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const StepArgs& a, const Tile* tiles, int n, int src_x, int dst_x, bool first,
-                          bool last, bool product, Coeffs cf, hipStream_t s) {
+hipError_t launch_combine(const StepArgs& a, const Tile* tiles, int n, int bm, int bn, int src_x, int dst_x,
+                          bool first, bool last, bool product, Coeffs cf, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  if (a.ns_dt == DT_BF16)
-    hipLaunchKernelGGL(k_combine_bf16, dim3(n), dim3(256), 0, s, a, tiles, n, src_x, dst_x, first ? 1 : 0,
-                       last ? 1 : 0, product ? 1 : 0, cf);
-  else
-    hipLaunchKernelGGL(k_combine_f32, dim3(n), dim3(256), 0, s, a, tiles, n, src_x, dst_x, first ? 1 : 0,
-                       last ? 1 : 0, product ? 1 : 0, cf);
+  const int f = first ? 1 : 0, l = last ? 1 : 0, p = product ? 1 : 0;
+  if (a.ns_dt != DT_BF16) {
+    if (bm != 128 || bn != 128) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_combine_f32, dim3(n), dim3(256), 0, s, a, tiles, n, src_x, dst_x, f, l, p, cf);
+    return hipGetLastError();
+  }
+#define MUON_COMB(BM, BN)                                                                                  \
+  if (last) hipLaunchKernelGGL((k_combine_bf16<BM, BN, true>), dim3(n), dim3(256), 0, s, a, tiles, n, src_x, \
+                               dst_x, f, p, cf);                                                           \
+  else hipLaunchKernelGGL((k_combine_bf16<BM, BN, false>), dim3(n), dim3(256), 0, s, a, tiles, n, src_x,    \
+                          dst_x, f, p, cf);
+  if (bm == 256 && bn == 256) {
+    MUON_COMB(256, 256)
+  } else if (bm == 128 && bn == 256) {
+    MUON_COMB(128, 256)
+  } else if (bm == 256 && bn == 128) {
+    MUON_COMB(256, 128)
+  } else if (bm == 128 && bn == 128) {
+    MUON_COMB(128, 128)
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef MUON_COMB
   return hipGetLastError();
 }
 

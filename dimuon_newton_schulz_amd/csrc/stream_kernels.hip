@@ -152,9 +152,11 @@ __global__ __launch_bounds__(256) void k_momentum(StepArgs a, const Tile* __rest
 }
 
 // ---------------------------------------------------------------------------
-// K2: energies from the partials (pairwise over blocks), then the factors.
-// One workgroup per matrix.  R, C are staged in the factor arrays, converted
-// in place once the maxima are known.
+// K2: Dimuon conditioning, over chunks of 256 elements of the padded row
+// range [0, round_up(m)) followed by the padded column range.  First the
+// energies (pairwise over the energy blocks, eight loads in flight) and the
+// chunk maxima; then, with the maxima of all chunks, the factors in place
+// (zero in the padding).
 // ---------------------------------------------------------------------------
 __device__ float block_max(float v, float* sh) {
   v = wave_max(v);
@@ -167,35 +169,80 @@ __device__ float block_max(float v, float* sh) {
   return r;
 }
 
-__global__ __launch_bounds__(256) void k_condition(StepArgs a, const uint16_t* __restrict__ mats) {
+__device__ __forceinline__ int64_t pad_up(int64_t x) { return (x + kPad - 1) / kPad * kPad; }
+
+__global__ __launch_bounds__(256) void k_cond_energy(StepArgs a, const Tile* __restrict__ tiles) {
   __shared__ float sh[8];
-  const int mat = mats[blockIdx.x];
-  const MatDesc& d = a.desc[mat];
+  const Tile t = tiles[blockIdx.x];
+  const MatDesc& d = a.desc[t.mat];
   const int m = d.m, n = d.n;
-  float* dr = reinterpret_cast<float*>(a.ws + d.dr_off);
-  float* dc = reinterpret_cast<float*>(a.ws + d.dc_off);
+  const int mp = static_cast<int>(pad_up(m));
+  const int idx = t.ti * 256 + threadIdx.x;
+  MUON_GLOBAL float* dr = gmem(reinterpret_cast<float*>(a.ws + d.dr_off));
+  MUON_GLOBAL float* dc = gmem(reinterpret_cast<float*>(a.ws + d.dc_off));
   const float* pr = reinterpret_cast<const float*>(a.ws + d.pr_off);
   const float* pc = reinterpret_cast<const float*>(a.ws + d.pc_off);
   float rmax = 0.0f, cmax = 0.0f;
-  for (int i = threadIdx.x; i < m; i += blockDim.x) {
-    float e = pairwise_strided(pr + i, d.ncb, m);
+  if (idx < mp) {
+    const int i = idx;
+    float e = 0.0f;
+    if (i < m) {
+      float f8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f8[j] = j < d.ncb ? gmem(pr)[static_cast<int64_t>(j) * m + i] : 0.0f;
+      e = pairwise_strided8(f8, pr + i, d.ncb, m);
+      if (d.energy_out) gmem(d.energy_out)[i] = e;
+    }
     dr[i] = e;
-    if (d.energy_out) d.energy_out[i] = e;
-    rmax = fmaxf(rmax, e);
-  }
-  for (int j = threadIdx.x; j < n; j += blockDim.x) {
-    float e = pairwise_strided(pc + j, d.nrb, n);
+    rmax = e;
+  } else if (idx < mp + pad_up(n)) {
+    const int j = idx - mp;
+    float e = 0.0f;
+    if (j < n) {
+      float f8[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) f8[q] = q < d.nrb ? gmem(pc)[static_cast<int64_t>(q) * n + j] : 0.0f;
+      e = pairwise_strided8(f8, pc + j, d.nrb, n);
+      if (d.energy_out) gmem(d.energy_out)[m + j] = e;
+    }
     dc[j] = e;
-    if (d.energy_out) d.energy_out[m + j] = e;
-    cmax = fmaxf(cmax, e);
+    cmax = e;
+  }
+  rmax = block_max(rmax, sh);
+  cmax = block_max(cmax, sh);
+  if (threadIdx.x == 0) {
+    MUON_GLOBAL float* cm = gmem(reinterpret_cast<float*>(a.ws + d.cm_off));
+    cm[2 * t.ti] = rmax;
+    cm[2 * t.ti + 1] = cmax;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_cond_factor(StepArgs a, const Tile* __restrict__ tiles) {
+  __shared__ float sh[8];
+  const Tile t = tiles[blockIdx.x];
+  const MatDesc& d = a.desc[t.mat];
+  const int m = d.m, n = d.n;
+  const int mp = static_cast<int>(pad_up(m));
+  const MUON_GLOBAL float* cm = gmem(reinterpret_cast<const float*>(a.ws + d.cm_off));
+  float rmax = 0.0f, cmax = 0.0f;
+  for (int c = threadIdx.x; c < d.ncond; c += blockDim.x) {
+    rmax = fmaxf(rmax, cm[2 * c]);
+    cmax = fmaxf(cmax, cm[2 * c + 1]);
   }
   rmax = block_max(rmax, sh);
   cmax = block_max(cmax, sh);
   // A zero previous momentum (all energies 0) switches the conditioning off.
   const bool on = rmax > 0.0f && cmax > 0.0f;
-  for (int i = threadIdx.x; i < m; i += blockDim.x) dr[i] = on ? cond_factor(dr[i], rmax, a.eps) : 1.0f;
-  for (int j = threadIdx.x; j < n; j += blockDim.x) dc[j] = on ? cond_factor(dc[j], cmax, a.eps) : 1.0f;
-  if (threadIdx.x == 0) a.scal[d.scal_idx].cond_on = on ? 1.0f : 0.0f;
+  const int idx = t.ti * 256 + threadIdx.x;
+  if (idx < mp) {
+    MUON_GLOBAL float* dr = gmem(reinterpret_cast<float*>(a.ws + d.dr_off));
+    if (idx < m) dr[idx] = on ? cond_factor(dr[idx], rmax, a.eps) : 1.0f;
+  } else if (idx < mp + pad_up(n)) {
+    MUON_GLOBAL float* dc = gmem(reinterpret_cast<float*>(a.ws + d.dc_off));
+    const int j = idx - mp;
+    if (j < n) dc[j] = on ? cond_factor(dc[j], cmax, a.eps) : 1.0f;
+  }
+  if (t.ti == 0 && threadIdx.x == 0) a.scal[d.scal_idx].cond_on = on ? 1.0f : 0.0f;
 }
 
 // ---------------------------------------------------------------------------
@@ -431,9 +478,15 @@ hipError_t launch_momentum(const StepArgs& a, const Tile* tiles, int n, bool ene
   return hipGetLastError();
 }
 
-hipError_t launch_condition(const StepArgs& a, const uint16_t* mats, int n, hipStream_t s) {
+hipError_t launch_cond_energy(const StepArgs& a, const Tile* tiles, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_condition, dim3(n), dim3(256), 0, s, a, mats);
+  hipLaunchKernelGGL(k_cond_energy, dim3(n), dim3(256), 0, s, a, tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_cond_factor(const StepArgs& a, const Tile* tiles, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_cond_factor, dim3(n), dim3(256), 0, s, a, tiles);
   return hipGetLastError();
 }
 
