@@ -27,6 +27,39 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 
+# HBM bytes per launch of the thin-path kernels on the LoRA batch, from two
+# rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per
+# dispatch), FETCH_SIZE scaled by 2.0 and WRITE_SIZE by 1.0: what the same
+# counters read for a 256 MiB device-to-device copy (--copy-probe).  Valid only
+# for the kernel sources they were taken on (sha256 of thin_kernel.hip and
+# common.h); the figures and the commands are in
+# profiles/k_thin_lora_batch_64x8x4096.md.
+THIN_SOURCES = ("dimuon_newton_schulz_amd/csrc/thin_kernel.hip", "dimuon_newton_schulz_amd/csrc/common.h")
+MEASURED_TRAFFIC = {
+    "sources_sha256": "32697b7238b4d9aff9566e76748a24b875e83658288ac2657f3f1457957761c8",
+    "k_thin_a": {"fetch_kib": 18232.7, "write_kib": 19013.2},
+    "k_thin_b": {"fetch_kib": 20441.0, "write_kib": 18496.1},
+}
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+
+
+def thin_sources_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in THIN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed counter runs, or None if the
+    kernel sources changed since they were taken."""
+    rec = MEASURED_TRAFFIC.get(kernel)
+    if rec is None or thin_sources_sha() != MEASURED_TRAFFIC["sources_sha256"]:
+        return None
+    return int(round((rec["fetch_kib"] * FETCH_SCALE + rec["write_kib"] * WRITE_SCALE) * 1024))
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -140,19 +173,26 @@ def measure(wl, steps, warmup, sets, ns_dtype=None):
         plans[i % sets].step()
         counts.append(lib.muon_set_launch_events(None, None, 0))
     torch.cuda.synchronize()
+    # Each event marker between two launches delays the next dispatch; the
+    # marker overhead per launch is the instrumented step time minus the
+    # plain one, spread over the step's launches, and is taken off each
+    # kernel's event interval.
+    hooked = sum(events[i * per_step].elapsed_time(events[i * per_step + counts[i] - 1]) for i in range(steps))
+    launches = sum(counts) - steps
+    overhead = max(0.0, hooked - ms * steps) / max(launches, 1)
     per_kind = {}
     for i in range(steps):
         base = i * per_step
         for j in range(1, counts[i]):
             kind = D.LAUNCH_KINDS[kinds[base + j]]
-            dt = events[base + j - 1].elapsed_time(events[base + j])
+            dt = max(events[base + j - 1].elapsed_time(events[base + j]) - overhead, 0.0)
             tot, n = per_kind.get(kind, (0.0, 0))
             per_kind[kind] = (tot + dt, n + 1)
     for p in plans:
         p.close()
     del plans
     torch.cuda.empty_cache()
-    return cfg, ms, per_kind
+    return cfg, ms, per_kind, overhead
 
 
 def roofline_for(wl, cfg, per_kind, work, steps):
@@ -165,7 +205,7 @@ def roofline_for(wl, cfg, per_kind, work, steps):
         nbytes = work[kind + "_bytes"]
         achieved = nbytes / (avg_ms * 1e-3) / 1e9
         return kind, {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic("k_" + kind),
                       "kernel": "k_" + kind, "avg_launch_ms": round(avg_ms, 5),
                       "bytes_per_launch": nbytes}
     flops = {"combine": work["comb_flops"], "gram": work["gram_flops"], "poly": work["poly_flops"]}.get(kind)
@@ -252,7 +292,7 @@ def main():
     work = algorithmic(wl, is_thin)
     full_count = wl.count
     sets = args.sets or (4 if work["hbm_bytes_min"] < 300e6 else 1)
-    cfg, ms, per_kind = measure(wl, args.steps, args.warmup, sets)
+    cfg, ms, per_kind, overhead = measure(wl, args.steps, args.warmup, sets)
     kind, roof = roofline_for(wl, cfg, per_kind, work, args.steps)
     total_flops = 5 * (work["gram_flops"] + work["poly_flops"] + work["comb_flops"])
     dtype = "f32" if (wl.w_dtype == "f32" and all(is_thin(*m.shape) for m in wl.mats)) else cfg.ns_dtype
@@ -276,6 +316,7 @@ def main():
         "step_gbs_algorithmic": round(work["hbm_bytes_min"] / (ms * 1e-3) / 1e9, 1),
         "roofline": roof,
         "kernel_ms_per_step": {k: round(v[0] / args.steps, 5) for k, v in sorted(per_kind.items())},
+        "event_marker_overhead_ms": round(overhead, 5),
     }
     if total_flops:
         out["ns_tflops_algorithmic"] = round(total_flops / (ms * 1e-3) / 1e12, 2)
@@ -288,7 +329,7 @@ def main():
             name, _, var = item.partition(":")
             wl2 = make_workload(name, dev, var or None)
             w2 = algorithmic(wl2, is_thin)
-            cfg2, ms2, pk2 = measure(wl2, args.extra_steps, 2, 1)
+            cfg2, ms2, pk2, _ = measure(wl2, args.extra_steps, 2, 1)
             k2, roof2 = roofline_for(wl2, cfg2, pk2, w2, args.extra_steps)
             tf = 5 * (w2["gram_flops"] + w2["poly_flops"] + w2["comb_flops"])
             extras.append({"workload": wl2.name, "variant": wl2.variant, "matrices": wl2.count,
