@@ -305,7 +305,7 @@ __device__ __forceinline__ void pair_group(const float (&y)[KP], TA w, TA (&acc)
 // Gram pairs reduced per pass: GP accumulators per thread stay live.
 template <int KP, typename TA>
 constexpr int gram_group() {
-  constexpr int cap = sizeof(TA) == 4 ? 36 : 18;
+  constexpr int cap = sizeof(TA) == 4 ? 18 : 9;
   return TS<KP>::NPAIR < cap ? TS<KP>::NPAIR : cap;
 }
 
@@ -435,10 +435,13 @@ __global__ __launch_bounds__(TT) void k_thin_energy(StepArgs args, const Tile* _
 // ---------------------------------------------------------------------------
 // Pass A
 // ---------------------------------------------------------------------------
-// TA: accumulation type of the per-thread Gram sums.
+// Pass A of a slice.  On return y holds M_t (stored), g the gradient,
+// dloc and sm.dglob the Dimuon factors (also written to the workspace for
+// pass B).  TA: accumulation type of the per-thread Gram sums.
 template <int KP, bool TALL, typename TA>
-__device__ __forceinline__ void pass_a_body(const StepArgs& args, const MatDesc& d, int s, int parity,
-                                            ThinSmem<KP>& sm) {
+__device__ __forceinline__ void pass_a_core(const StepArgs& args, const MatDesc& d, int s, int parity,
+                                            ThinSmem<KP>& sm, bool full, float (&y)[KP][TS<KP>::VEC],
+                                            float (&g)[KP][TS<KP>::VEC], float (&dloc)[TS<KP>::VEC]) {
   constexpr int VEC = TS<KP>::VEC, L = TS<KP>::L, NPAIR = TS<KP>::NPAIR;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k = d.k, N = d.N, n = d.n;
@@ -457,14 +460,10 @@ __device__ __forceinline__ void pass_a_body(const StepArgs& args, const MatDesc&
     for (int e = 0; e < VEC; ++e) pe[e] = (l0 + e < N) ? gmem(cin.pos)[l0 + e] : 0.0f;
   }
 
-  const bool full = slice_full<KP, TALL>(k, N, n, s);
-  float y[KP][VEC];   // M_{t-1}, then M_t, then Y
-  float g[KP][VEC];
-  slice_load<KP, TALL>(d.mom, args.mom_dt, k, N, n, l0, full, y);
+  slice_load<KP, TALL>(d.mom, args.mom_dt, k, N, n, l0, full, y);   // M_{t-1}, then M_t
   slice_load<KP, TALL>(d.g, args.g_dt, k, N, n, l0, full, g);
 
   // ---- Dimuon factors from the energies of M_{t-1} --------------------------
-  float dloc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) dloc[e] = 1.0f;
   if (dimuon) {
@@ -500,18 +499,17 @@ __device__ __forceinline__ void pass_a_body(const StepArgs& args, const MatDesc&
     for (int e = 0; e < VEC; ++e) y[a][e] = momentum_value(args.mu, y[a][e], g[a][e], args.mom_dt);
   slice_store<KP, TALL>(d.mom, args.mom_dt, k, N, n, l0, full, y);
 
-  // ---- Y = D_glob V D_loc -----------------------------------------------------
-  if (args.nesterov) {
+  // ---- Y = D_glob V D_loc (V = M_t, or G + mu M_t with Nesterov) -----------
+  float v[KP][VEC];
 #pragma unroll
-    for (int a = 0; a < KP; ++a)
+  for (int a = 0; a < KP; ++a)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) y[a][e] = g[a][e] + args.mu * y[a][e];
-  }
+    for (int e = 0; e < VEC; ++e) v[a][e] = args.nesterov ? g[a][e] + args.mu * y[a][e] : y[a][e];
   if (dimuon) {
 #pragma unroll
     for (int a = 0; a < KP; ++a)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) y[a][e] = (sm.dglob[a] * y[a][e]) * dloc[e];
+      for (int e = 0; e < VEC; ++e) v[a][e] = (sm.dglob[a] * v[a][e]) * dloc[e];
     MUON_GLOBAL float* tdl = gmem(reinterpret_cast<float*>(args.ws + d.tdl_off));
 #pragma unroll
     for (int e = 0; e < VEC; ++e)
@@ -524,12 +522,20 @@ __device__ __forceinline__ void pass_a_body(const StepArgs& args, const MatDesc&
     constexpr int GP = gram_group<KP, TA>(), NG = (NPAIR + GP - 1) / GP;
     MUON_GLOBAL double* tg = gmem(reinterpret_cast<double*>(args.ws + d.tg_off)) + static_cast<int64_t>(s) * NPAIR;
     MUON_GLOBAL double* tg2 = gmem(reinterpret_cast<double*>(args.ws + d.tg2_off)) + static_cast<int64_t>(s) * NPAIR;
-    gram_slice<TA, KP, 0, NG>(y, dloc, dimuon, tg, tg2, sm);
+    gram_slice<TA, KP, 0, NG>(v, dloc, dimuon, tg, tg2, sm);
   }
 }
 
 // The orthogonaliser's precision sets the Gram's: float32 per-thread sums
 // when the Newton-Schulz products are bf16, float64 in fp32 mode.
+template <int KP, bool TALL, typename TA>
+__device__ __forceinline__ void pass_a_body(const StepArgs& args, const MatDesc& d, int s, int parity,
+                                            ThinSmem<KP>& sm) {
+  constexpr int VEC = TS<KP>::VEC;
+  float y[KP][VEC], g[KP][VEC], dloc[VEC];
+  pass_a_core<KP, TALL, TA>(args, d, s, parity, sm, slice_full<KP, TALL>(d.k, d.N, d.n, s), y, g, dloc);
+}
+
 template <int KP, typename TA>
 __global__ __launch_bounds__(TT, 4) void k_thin_a(StepArgs args, const Tile* __restrict__ tiles, int parity) {
   __shared__ ThinSmem<KP> sm;
@@ -678,6 +684,75 @@ __device__ __forceinline__ void gram_norms(ThinSmem<KP>& sm, double inv_nu) {
   lds_barrier();
 }
 
+// The end of pass B, once sm.sQ holds Q_5 and sm.sG, sm.sG2 the Grams: the
+// norm fix, the energies of M_t (in y) for the next step, Z = (Q/nu) Y, O
+// and the update of W (in w).  dg is d_glob[tid] for tid < KP.
+template <int KP, bool TALL>
+__device__ __forceinline__ void pass_b_tail(const StepArgs& args, const MatDesc& d, int s, int parity,
+                                            ThinSmem<KP>& sm, bool full, double inv_nu, float dg,
+                                            float (&y)[KP][TS<KP>::VEC], float (&w)[KP][TS<KP>::VEC],
+                                            const float (&g)[KP][TS<KP>::VEC], const float (&dloc)[TS<KP>::VEC]) {
+  constexpr int VEC = TS<KP>::VEC, L = TS<KP>::L;
+  const int tid = threadIdx.x;
+  const int k = d.k, N = d.N, n = d.n;
+  const int l0 = s * L + tid * VEC;
+  const bool dimuon = args.dimuon != 0;
+  for (int e = tid; e < KP * KP; e += TT) sm.sQf[e] = static_cast<float>(sm.sQ[e] * inv_nu);
+  if (tid < KP) sm.dglob[tid] = dg;   // read after the next barrier
+  if (dimuon) {
+    gram_norms<KP>(sm, inv_nu);
+    if (tid == 0) sm.post = (sm.nrm[1] == 0.0) ? 0.0f : static_cast<float>(sqrt(sm.nrm[0]) / sqrt(sm.nrm[1]));
+  } else if (tid == 0) {
+    sm.post = 1.0f;
+  }
+  lds_barrier();
+
+  // ---- energies of M_t for the next step's conditioning --------------------
+  if (dimuon) energies_to_cache<KP>(y, d, s, l0, cache_of(args, d, parity ^ 1), sm);
+
+  // ---- Y, Z = Qs Y, O, update ------------------------------------------------
+  if (args.nesterov) {
+#pragma unroll
+    for (int a = 0; a < KP; ++a)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) y[a][e] = g[a][e] + args.mu * y[a][e];
+  }
+  if (dimuon) {
+#pragma unroll
+    for (int a = 0; a < KP; ++a)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) y[a][e] = (sm.dglob[a] * y[a][e]) * dloc[e];
+  }
+  {
+    float z[KP][VEC];
+#pragma unroll
+    for (int a = 0; a < KP; ++a) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) z[a][e] = 0.0f;
+#pragma unroll
+      for (int b = 0; b < KP; ++b) {
+        const float qab = sm.sQf[a * KP + b];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) z[a][e] = __builtin_fmaf(qab, y[b][e], z[a][e]);
+      }
+      // One row of Q live at a time (all rows hoisted would take KP^2 registers).
+      if constexpr (KP >= 8) __builtin_amdgcn_sched_barrier(0);
+    }
+    const float post = sm.post;
+#pragma unroll
+    for (int a = 0; a < KP; ++a)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float ov = dimuon ? post * ((sm.dglob[a] * z[a][e]) * dloc[e]) : z[a][e];
+        y[a][e] = ov;
+        const float upd = __builtin_fmaf(d.update_scale, ov, args.weight_decay * w[a][e]);
+        w[a][e] = __builtin_fmaf(-args.lr, upd, w[a][e]);
+      }
+  }
+  slice_store<KP, TALL>(d.w, args.w_dt, k, N, n, l0, full, w);
+  if (d.o_out) slice_store<KP, TALL>(d.o_out, DT_F32, k, N, n, l0, full, y);
+}
+
 template <int KP, bool TALL>
 __device__ __forceinline__ void pass_b_body(const StepArgs& args, const MatDesc& d, int s, int ns_steps,
                                             const ThinCoeffs& cf, int parity, ThinSmem<KP>& sm) {
@@ -768,59 +843,7 @@ __device__ __forceinline__ void pass_b_body(const StepArgs& args, const MatDesc&
   } else {
     lds_barrier();
   }
-  const double inv_nu = inv_norm();
-  for (int e = tid; e < KP * KP; e += TT) sm.sQf[e] = static_cast<float>(sm.sQ[e] * inv_nu);
-  if (tid < KP) sm.dglob[tid] = dg;   // read after the next barrier
-  if (dimuon) {
-    gram_norms<KP>(sm, inv_nu);
-    if (tid == 0) sm.post = (sm.nrm[1] == 0.0) ? 0.0f : static_cast<float>(sqrt(sm.nrm[0]) / sqrt(sm.nrm[1]));
-  } else if (tid == 0) {
-    sm.post = 1.0f;
-  }
-  lds_barrier();
-
-  // ---- energies of M_t for the next step's conditioning --------------------
-  if (dimuon) energies_to_cache<KP>(y, d, s, l0, cache_of(args, d, parity ^ 1), sm);
-
-  // ---- Y, Z = Qs Y, O, update ------------------------------------------------
-  if (args.nesterov) {
-#pragma unroll
-    for (int a = 0; a < KP; ++a)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) y[a][e] = g[a][e] + args.mu * y[a][e];
-  }
-  if (dimuon) {
-#pragma unroll
-    for (int a = 0; a < KP; ++a)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) y[a][e] = (sm.dglob[a] * y[a][e]) * dloc[e];
-  }
-  {
-    float z[KP][VEC];
-#pragma unroll
-    for (int a = 0; a < KP; ++a) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) z[a][e] = 0.0f;
-#pragma unroll
-      for (int b = 0; b < KP; ++b) {
-        const float qab = sm.sQf[a * KP + b];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) z[a][e] = __builtin_fmaf(qab, y[b][e], z[a][e]);
-      }
-    }
-    const float post = sm.post;
-#pragma unroll
-    for (int a = 0; a < KP; ++a)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float ov = dimuon ? post * ((sm.dglob[a] * z[a][e]) * dloc[e]) : z[a][e];
-        y[a][e] = ov;
-        const float upd = __builtin_fmaf(d.update_scale, ov, args.weight_decay * w[a][e]);
-        w[a][e] = __builtin_fmaf(-args.lr, upd, w[a][e]);
-      }
-  }
-  slice_store<KP, TALL>(d.w, args.w_dt, k, N, n, l0, full, w);
-  if (d.o_out) slice_store<KP, TALL>(d.o_out, DT_F32, k, N, n, l0, full, y);
+  pass_b_tail<KP, TALL>(args, d, s, parity, sm, full, inv_norm(), dg, y, w, g, dloc);
 }
 
 template <int KP>

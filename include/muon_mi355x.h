@@ -150,7 +150,7 @@ muon_status_t dimuon_step(const muon_matrix_t* mats, int64_t count,
 /* Kernel kinds reported by the launch-event hook. */
 typedef enum muon_launch_kind {
   MUON_LAUNCH_START = -1,     /* event recorded before the first launch */
-  MUON_LAUNCH_THIN = 0,       /* thin path pass B: k x k iteration, apply, update */
+  MUON_LAUNCH_THIN = 0,       /* thin path pass B: k x k iteration, next energies, apply, update */
   MUON_LAUNCH_MOMENTUM = 1,   /* momentum (+ energy partials) */
   MUON_LAUNCH_CONDITION = 2,  /* energies -> Dimuon factors */
   MUON_LAUNCH_PRESCALE = 3,   /* conditioned, normalised bf16/f32 copy (+ transpose) */
@@ -161,7 +161,7 @@ typedef enum muon_launch_kind {
   MUON_LAUNCH_POSTNORM = 8,   /* Dimuon norm fix */
   MUON_LAUNCH_UPDATE = 9,     /* O and the weight update */
   MUON_LAUNCH_THIN_ENERGY = 10, /* thin path: energies of M_{t-1} (no cached energies) */
-  MUON_LAUNCH_THIN_A = 11     /* thin path pass A: momentum, next energies, Gram partials */
+  MUON_LAUNCH_THIN_A = 11     /* thin path pass A: momentum, Gram partials */
 } muon_launch_kind_t;
 
 /* Timing hook, per host thread; not part of the method.  When `events` is

@@ -4,6 +4,7 @@ Each case prints its name, shapes and variant before touching the GPU.
 Inputs come from the seeded generators in ``workloads``; expected values
 come only from ``oracle``."""
 
+import ctypes
 import sys
 
 import numpy as np
@@ -41,8 +42,27 @@ def run_case(wl, variant, cfg, indices=None, scales=None, o_tol=None):
     return gpu, errs
 
 
+def launch_kinds(step):
+    """Kinds of the kernel launches one call of step() makes (the library's launch-event hook)."""
+    lib = D.load_library()
+    cap = 64
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(cap)]
+    for e in events:
+        e.record()
+    torch.cuda.synchronize()
+    handles = (ctypes.c_void_p * cap)(*[e.cuda_event for e in events])
+    kinds = (ctypes.c_int32 * cap)()
+    lib.muon_set_launch_events(handles, kinds, cap)
+    try:
+        step()
+    finally:
+        n = lib.muon_set_launch_events(None, None, 0)
+    torch.cuda.synchronize()
+    return [D.LAUNCH_KINDS[kinds[i]] for i in range(1, n)]
+
+
 # ---------------------------------------------------------------------------
-# Thin path (Gram side <= 32): one kernel per batch
+# Thin path (Gram side <= 32): two launches per padded Gram side
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("variant", ["muon", "dimuon"])
@@ -65,6 +85,20 @@ def test_thin_ragged_shapes(shape, variant):
     for dt in ("f32", "bf16"):
         wl = W.random_batch([shape], dtype=dt, ns_dtype="f32", seed=hash(shape) % 97, variant=variant)
         run_case(wl, variant, cfg_of(wl))
+
+
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
+def test_thin_large_batch(variant):
+    # 150 LoRA pairs: 2400 slices, more workgroups than the GPU holds at once.
+    wl = W.lora_batch(pairs=150, rank=8, d=4096, seed=3)
+    cfg = cfg_of(wl)
+    params = [D.Param(w=m.w.cuda(), g=m.g.cuda(), mom=m.m_prev.cuda()) for m in wl.mats]
+    fn = D.dimuon_step if variant == "dimuon" else D.muon_step
+    announce(f"{wl.name} {variant}: launch kinds")
+    kinds = launch_kinds(lambda: fn(params, cfg))
+    assert kinds.count("thin_a") == 1 and kinds.count("thin_b") == 1, kinds
+    del params
+    run_case(wl, variant, cfg, indices=[0, 1, wl.count // 2, wl.count - 1])
 
 
 # ---------------------------------------------------------------------------
