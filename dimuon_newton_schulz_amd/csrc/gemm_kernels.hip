@@ -4,28 +4,26 @@
 // operands row-major and K-contiguous.  This works because the workspace
 // keeps each iterate in both layouts, X (k x N) and X^T (N x k):
 //   Gram     A = X X^T        P = X,   Q = X     (K = N)   symmetric
-//   poly     B = b A + c A A  P = A,   Q = A     (K = k)   symmetric
-//   combine  X' = a X + B X   P = B,   Q = X^T   (K = k)
+//   poly     B = a I + b A + c A A   P = A, Q = A   (K = k)   symmetric
+//   combine  X' = B X                P = B, Q = X^T (K = k)
+// (a X + (b A + c A A) X with the a X term folded into B's diagonal, so the
+// combine reads nothing but its two operands.)
 // The symmetric products compute the upper-triangular tiles only and store
 // each such tile and its mirror.  The combine stores X' and X'^T.
 //
 // bf16 path: a BM x BN workgroup tile (BM, BN in {128, 256}), four wave64 in
 // a 2 x 2 grid, each wave owning (BM/2) x (BN/2) as 32 x 32 blocks of
 // v_mfma_f32_32x32x16_bf16.  Operands go from global memory straight into a
-// ring of four LDS stages of 32 k-values (global_load_lds_dwordx4, no
-// register staging), so three stages are in flight while one is multiplied
-// (the loop is pipelined so that LDS fragment reads are covered by MFMAs):
-// a 256 x 256 tile keeps 96 KB of loads outstanding per CU, enough to cover
-// the latency of L2 and HBM under a full chip of GEMM traffic.  A 256 x 256
+// ring of LDS stages of 32 k-values (global_load_lds_dwordx4, no register
+// staging); all stages but the one being multiplied are in flight (the loop
+// is pipelined so that LDS fragment reads are covered by MFMAs).  A 256 x 256
 // tile reads half as many LDS bytes per MFMA as a 128 x 128 one and needs half
-// the L2 traffic per flop; with 128 KB of LDS and 256 accumulator registers
+// the L2 traffic per flop; with its 160 KB ring and 256 accumulator registers
 // one workgroup runs per CU (two for 128 x 128).
 //
-// Epilogue without LDS: lane l of a 32 x 32 block holds, for each group of
-// four accumulators, rows i..i+3 of column j = l mod 32.  Those are
-// contiguous in the transposed output, which is written directly; for the
-// row-major output, the four lanes of a quad (four consecutive columns)
-// exchange values with DPP so that each holds one row's four columns.
+// The epilogue stages the fp32 accumulators through LDS (transposed, half a
+// tile per round) so that both the row-major and the transposed outputs are
+// written as 16-byte runs.
 #include <type_traits>
 
 #include "common.h"
@@ -36,19 +34,24 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int LBK = 32;   // k per pipeline stage
-constexpr int NSTG = 4;   // LDS stages: three in flight while one is multiplied
 
+// Ring depth: the main loop is bound by the operand bytes each CU keeps in
+// flight, and the LDS ring is the only buffer, so the ring takes all the LDS
+// a workgroup may have: 160 KB for 256 x 256 (five stages, four in flight),
+// 144 KB for 128 x 256, and 80 KB for 128 x 128 (two workgroups per CU).
 template <int BM, int BN>
 struct GemmT {
   static constexpr int MS = BM / 64, NS = BN / 64;   // 32 x 32 blocks per wave
   static constexpr int LA = BM / 64, LB = BN / 64;   // 16-byte LDS loads per thread and stage
   static constexpr int LPS = LA + LB;
   static constexpr int STAGE = (BM + BN) * LBK;      // bf16 elements per stage: A rows, then B rows
+  static constexpr int NSTG = BM + BN == 384 ? 6 : 5;
   static constexpr int SP = BM / 2 + 2;              // epilogue staging row stride (floats)
   union Smem {
     uint16_t buf[NSTG][STAGE];
     float st[BN * SP];                               // half a tile, transposed, fp32
   };
+  static_assert(sizeof(Smem) <= (BM * BN == 16384 ? 81920 : 163840), "LDS budget");
 };
 
 // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous
@@ -92,16 +95,29 @@ __device__ __forceinline__ void issue_stage(const MUON_GLOBAL uint16_t* P, int64
   }
 }
 
+// Waits until at most min(n, G) groups of LPS loads are outstanding (n is
+// uniform across the wave).
+template <int LPS, int G>
+__device__ __forceinline__ void wait_groups(int n) {
+  if constexpr (G == 0) {
+    wait_vm<0>();
+  } else {
+    if (n >= G) wait_vm<G * LPS>();
+    else wait_groups<LPS, G - 1>(n);
+  }
+}
+
 // acc[s][t] += P[rows wr*BM/2 + s*32 ..][k] * Q[rows wc*BN/2 + t*32 ..][k] over k < K
-// (K a multiple of 4 * LBK).  A stage holds two k-halves of 16.  Iteration kt:
+// (K a multiple of 4 * LBK).  A stage holds two k-halves of 16; S = NSTG.
+// Iteration kt:
 //   read half 1 of stage kt;  MFMAs of half 0 (read in the previous iteration)
 //   wait for this wave's loads of stage kt+1; barrier
-//   load stage kt+4 into stage kt's buffer (every wave has its fragments of
+//   load stage kt+S into stage kt's buffer (every wave has its fragments of
 //   stage kt in registers: LDS reads complete before the barrier)
 //   read half 0 of stage kt+1;  MFMAs of half 1
-// so fragment reads are always covered by MFMAs, and three stages are in
-// flight while one is multiplied.  The first four stages are issued before
-// the loop.
+// so fragment reads are always covered by MFMAs, and S-1 stages are in
+// flight while one is multiplied.  The first S stages are issued before the
+// loop.
 template <int BM, int BN>
 __device__ __forceinline__ void mma_nt_bf16(const uint16_t* Pg, int64_t ldp, const uint16_t* Qg, int64_t ldq,
                                             int K, typename GemmT<BM, BN>::Smem& sm,
@@ -112,6 +128,7 @@ __device__ __forceinline__ void mma_nt_bf16(const uint16_t* Pg, int64_t ldp, con
   const int wr = wave >> 1, wc = wave & 1;
   const MUON_GLOBAL uint16_t* P = gmem(Pg);
   const MUON_GLOBAL uint16_t* Q = gmem(Qg);
+  constexpr int NSTG = G::NSTG;
   const int nk = K / LBK;
 #pragma unroll
   for (int st = 0; st < NSTG; ++st)
@@ -135,11 +152,8 @@ __device__ __forceinline__ void mma_nt_bf16(const uint16_t* Pg, int64_t ldp, con
       for (int t = 0; t < NS; ++t)
         acc[s][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s], fb[t], acc[s][t], 0, 0, 0);
   };
-  // Stage 0 landed (loads issued after it: stages 1 .. 3, if any).
-  if (nk >= 4) wait_vm<3 * LPS>();
-  else if (nk == 3) wait_vm<2 * LPS>();
-  else if (nk == 2) wait_vm<LPS>();
-  else wait_vm<0>();
+  // Stage 0 landed (loads issued after it: stages 1 .. S-1, if any).
+  wait_groups<LPS, NSTG - 1>(nk - 1);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   read_half(sm.buf[0], ch0, fa0, fb0);
@@ -150,11 +164,8 @@ __device__ __forceinline__ void mma_nt_bf16(const uint16_t* Pg, int64_t ldp, con
     // (The scheduling barriers keep the MFMAs on their side of the wait.)
     __builtin_amdgcn_sched_barrier(0);
     // This wave's reads of stage kt are complete; stage kt+1 has landed.
-    const int left = nk - 2 - kt;   // stages issued after kt+1
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    if (left >= 2) wait_vm<2 * LPS>();
-    else if (left == 1) wait_vm<LPS>();
-    else wait_vm<0>();
+    wait_groups<LPS, NSTG - 2>(nk - 2 - kt);   // stages issued after kt+1: up to kt+S-1
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     __builtin_amdgcn_sched_barrier(0);
@@ -360,29 +371,37 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(StepArgs a, const Tile* __
   auto aux_n = [&](int i, int j0) {
     return kind == 1 ? fetch8_bf16(E, (gi0 + i) * ldo + gj0 + j0) : make_uint4(0, 0, 0, 0);
   };
-  auto fin = [&](float (&v)[8], const uint4& aux) {
+  // Polynomial: c (A A) + b A, plus a on the diagonal.  Only diagonal tiles
+  // hold diagonal elements; in a run of eight, element e is on it iff
+  // e == e_diag (out of 0..7 otherwise).
+  const bool diag_tile = kind == 1 && t.ti == t.tj;
+  auto fin = [&](float (&v)[8], const uint4& aux, int e_diag) {
     float e8[8];
     unpack8_bf16(aux, e8);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = kind == 1 ? alpha * v[e] + cf.b * e8[e] : alpha * v[e];
+    for (int e = 0; e < 8; ++e) {
+      v[e] = kind == 1 ? alpha * v[e] + cf.b * e8[e] : alpha * v[e];
+      if (kind == 1) v[e] += e == e_diag ? cf.a : 0.0f;
+    }
   };
   auto out_t = [&](int j, int i0, float (&v)[8], const uint4& aux) {
-    fin(v, aux);
+    fin(v, aux, diag_tile ? j - i0 : -1);
     store8(dst, (gj0 + j) * ldo + gi0 + i0, DT_BF16, v);
   };
   auto out_n = [&](int i, int j0, float (&v)[8], const uint4& aux) {
-    fin(v, aux);
+    fin(v, aux, diag_tile ? i - j0 : -1);
     store8(dst, (gi0 + i) * ldo + gj0 + j0, DT_BF16, v);
   };
   staged_epilogue<BT, BT>(acc, sm, true, t.ti != t.tj, aux_t, aux_n, out_t, out_n);
 }
 
 // ---------------------------------------------------------------------------
-// Combine (bf16 operands): X' = alpha (a X + B X).
+// Combine (bf16 operands): X' = alpha B X, with B = a I + b A + c A A.
+// XTERM (no iterations: Z = alpha a X): the product is skipped and X read.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, bool LAST>
+template <int BM, int BN, bool LAST, bool XTERM>
 __global__ __launch_bounds__(256, 1) void k_combine_bf16(StepArgs a, const Tile* __restrict__ tiles, int ntiles,
-                                                      int src_x, int dst_x, int first, int product, Coeffs cf) {
+                                                      int src_x, int dst_x, int first, Coeffs cf) {
   constexpr bool last = LAST;
   using G = GemmT<BM, BN>;
   __shared__ typename G::Smem sm;
@@ -397,7 +416,7 @@ __global__ __launch_bounds__(256, 1) void k_combine_bf16(StepArgs a, const Tile*
     for (int u = 0; u < G::NS; ++u)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[s][u][r] = 0.0f;
-  if (product)
+  if constexpr (!XTERM)
     mma_nt_bf16<BM, BN>(Bm + static_cast<int64_t>(t.ti) * BM * d.KP, d.KP,
                         XT + static_cast<int64_t>(t.tj) * BN * d.KP, d.KP, d.KP, sm, acc);
 
@@ -427,14 +446,21 @@ __global__ __launch_bounds__(256, 1) void k_combine_bf16(StepArgs a, const Tile*
     sz = sz + v * v;
     sp = sp + p * p;
   };
-  // X[i][j] = X^T[j][i]: column runs read X^T, row runs read X.
-  auto aux_t = [&](int j, int i0) { return fetch8_bf16(XT, (gj0 + j) * d.KP + gi0 + i0); };
-  auto aux_n = [&](int i, int j0) { return fetch8_bf16(X, (gi0 + i) * d.NP + gj0 + j0); };
-  auto out_t = [&](int j, int i0, float (&v)[8], const uint4& aux) {
+  // X[i][j] = X^T[j][i]: column runs read X^T, row runs read X (XTERM only).
+  auto aux_t = [&](int j, int i0) {
+    return XTERM ? fetch8_bf16(XT, (gj0 + j) * d.KP + gi0 + i0) : make_uint4(0, 0, 0, 0);
+  };
+  auto aux_n = [&](int i, int j0) {
+    return XTERM ? fetch8_bf16(X, (gi0 + i) * d.NP + gj0 + j0) : make_uint4(0, 0, 0, 0);
+  };
+  auto fin = [&](float (&v)[8], const uint4& aux) {
     float x[8];
     unpack8_bf16(aux, x);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = alpha * (cf.a * x[e] + v[e]);
+    for (int e = 0; e < 8; ++e) v[e] = XTERM ? alpha * (cf.a * x[e]) : alpha * v[e];
+  };
+  auto out_t = [&](int j, int i0, float (&v)[8], const uint4& aux) {
+    fin(v, aux);
     if (LAST && partials) {
       float fr[8];
       factors8(dgr, gi0 + i0, fr);
@@ -445,10 +471,7 @@ __global__ __launch_bounds__(256, 1) void k_combine_bf16(StepArgs a, const Tile*
     store8(dst_t, (gj0 + j) * d.KP + gi0 + i0, odt, v);
   };
   auto out_n = [&](int i, int j0, float (&v)[8], const uint4& aux) {
-    float x[8];
-    unpack8_bf16(aux, x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = alpha * (cf.a * x[e] + v[e]);
+    fin(v, aux);
     if (LAST && partials) {
       float fc[8];
       factors8(dgc, gj0 + j0, fc);
@@ -659,11 +682,18 @@ hipError_t launch_combine(const StepArgs& a, const Tile* tiles, int n, int bm, i
     hipLaunchKernelGGL(k_combine_f32, dim3(n), dim3(256), 0, s, a, tiles, n, src_x, dst_x, f, l, p, cf);
     return hipGetLastError();
   }
-#define MUON_COMB(BM, BN)                                                                                  \
-  if (last) hipLaunchKernelGGL((k_combine_bf16<BM, BN, true>), dim3(n), dim3(256), 0, s, a, tiles, n, src_x, \
-                               dst_x, f, p, cf);                                                           \
-  else hipLaunchKernelGGL((k_combine_bf16<BM, BN, false>), dim3(n), dim3(256), 0, s, a, tiles, n, src_x,    \
-                          dst_x, f, p, cf);
+#define MUON_COMB(BM, BN)                                                                                   \
+  if (!product) {                                                                                            \
+    if (!last) return hipErrorInvalidValue;                                                                  \
+    hipLaunchKernelGGL((k_combine_bf16<BM, BN, true, true>), dim3(n), dim3(256), 0, s, a, tiles, n, src_x,   \
+                       dst_x, f, cf);                                                                        \
+  } else if (last) {                                                                                         \
+    hipLaunchKernelGGL((k_combine_bf16<BM, BN, true, false>), dim3(n), dim3(256), 0, s, a, tiles, n, src_x,  \
+                       dst_x, f, cf);                                                                        \
+  } else {                                                                                                   \
+    hipLaunchKernelGGL((k_combine_bf16<BM, BN, false, false>), dim3(n), dim3(256), 0, s, a, tiles, n, src_x, \
+                       dst_x, f, cf);                                                                        \
+  }
   if (bm == 256 && bn == 256) {
     MUON_COMB(256, 256)
   } else if (bm == 128 && bn == 256) {

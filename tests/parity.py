@@ -107,10 +107,12 @@ def check_matrix(gpu: GpuResult, ref, i: int, cfg, variant: str, wl, scale: floa
             scale_out = _post_scale(ref) * ref.d_r[:, None] * ref.d_c[None, :]
         err = np.max(np.abs(o_g - o_r) / scale_out)
         tol = TOL_BF16_MAXABS if o_tol is None else o_tol
+        print(f"[parity] {ctx}: max|dO| = {err:.3e} (tol {tol})", flush=True)
         assert err <= tol, f"{ctx}: max|dO| = {err:.3e} > {tol}"
     else:
         err = np.linalg.norm(o_g - o_r) / max(np.linalg.norm(o_r), 1e-300)
         tol = TOL_F32_REL if o_tol is None else o_tol
+        print(f"[parity] {ctx}: rel ||dO|| = {err:.3e} (tol {tol})", flush=True)
         assert err <= tol, f"{ctx}: rel ||dO|| = {err:.3e} > {tol}"
     # Momentum: the correctly rounded value of mu * M_prev + G, bit for bit.
     np.testing.assert_array_equal(gpu.m[i], ref.m, err_msg=f"{ctx}: momentum")
