@@ -34,6 +34,7 @@
 // of the stated pairwise tree.
 #pragma clang fp contract(off)
 
+#include <type_traits>
 #include <utility>
 
 #include "common.h"
@@ -239,13 +240,29 @@ __device__ __forceinline__ EnergyCache cache_of(const StepArgs& a, const MatDesc
   return {base, base + static_cast<int64_t>(d.S) * d.KP, base + static_cast<int64_t>(d.S) * d.KP + d.N};
 }
 
+// Slices up to which pass A uses the matrix-core Gram: four workgroups per
+// CU on 256 CUs, the most that run in one round.
+constexpr int kThinMfmaGramSlices = 1024;
+
+// Gram sides that take the matrix-core Gram in bf16 mode: below 8 the
+// per-thread sums are cheap, and from 16 the fp32 staging would cost both
+// passes a workgroup per CU (shared memory).  fp32 mode keeps float64 sums.
+template <int KP>
+constexpr bool gram_on_mfma() { return KP == 8; }
+
 template <int KP>
 struct ThinSmem {
   static constexpr int GP = TS<KP>::NPAIR < 36 ? TS<KP>::NPAIR : 36;   // largest Gram pair group
-  union {                          // 16-lane row sums of a Gram pass (wave, row)
-    double d[NWV * 4][GP];
-    float f[NWV * 4][GP];
-  } gred;
+  static constexpr bool MF = gram_on_mfma<KP>();
+  static constexpr int LP = MF ? TT + 4 : 1;                           // staged row length (floats)
+  union {
+    union {                        // 16-lane row sums of a Gram pass (wave, row)
+      double d[NWV * 4][GP];
+      float f[NWV * 4][GP];
+    } gred;
+    float sy[2][KP][LP];                         // matrix-core Gram: Y and d_loc^2 Y rows
+    float sred[NWV][MF ? 2 * KP : 1][MF ? KP : 1];   // matrix-core Gram: each wave's [plain; weighted] x plain
+  };
   float red[NWV][KP];
   float fred[NWV];
   float rg[KP], dglob[KP];
@@ -366,6 +383,73 @@ __device__ __forceinline__ void gram_slice(const float (&y)[KP][TS<KP>::VEC], co
   }
 }
 
+typedef float tf32x4_t __attribute__((ext_vector_type(4)));
+
+// The slice's Gram partials on the matrix cores (Gram side 8, bf16 mode):
+// both Grams are one product over the slice's positions,
+//   [Y; D^2 Y] (2KP x L) times Y^T (L x KP),   D = diag(d_loc),
+// in fp32 (v_mfma_f32_16x16x4_f32: products exact, sums in fp32, like the
+// per-thread sums it replaces).  Y and D^2 Y are staged in LDS as rows
+// (padded by 16 bytes against bank conflicts), one position per thread per
+// round (VEC rounds, so the staging takes the LDS of 256 positions); each
+// wave multiplies a quarter of a round's positions, and the four waves'
+// results are added in double at the end.  In a group of four products,
+// lane l supplies operand row (l mod 16) at positions 4 (l / 16) .. + 3 of the
+// group's 16, one per product, so every position meets itself in both
+// operands exactly once.
+template <int KP>
+__device__ __forceinline__ void gram_slice_mfma(const float (&v)[KP][TS<KP>::VEC], const float (&dl)[TS<KP>::VEC],
+                                                bool two, MUON_GLOBAL double* out, MUON_GLOBAL double* out2,
+                                                ThinSmem<KP>& sm) {
+  constexpr int VEC = TS<KP>::VEC, NPAIR = TS<KP>::NPAIR;
+  constexpr int PW = TT / NWV;   // positions per wave and round
+  static_assert(KP == 8, "one 16-row product: [plain; weighted]");
+  static_assert(PW % 16 == 0, "slice geometry");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 15, kq = lane >> 4;
+  const float* pa = i < KP ? sm.sy[0][i] : sm.sy[1][i - KP];
+  const float* pb = sm.sy[0][i % KP];
+  tf32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    if (e > 0) lds_barrier();   // the previous round's reads are done
+#pragma unroll
+    for (int a = 0; a < KP; ++a) {
+      sm.sy[0][a][tid] = v[a][e];
+      if (two) sm.sy[1][a][tid] = v[a][e] * (dl[e] * dl[e]);
+    }
+    lds_barrier();
+#pragma unroll
+    for (int g = 0; g < PW / 16; ++g) {
+      const int p = wave * PW + g * 16 + kq * 4;
+      const float4 fb = *reinterpret_cast<const float4*>(pb + p);
+      const float4 fa = *reinterpret_cast<const float4*>(pa + p);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.x, fb.x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.y, fb.y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.z, fb.z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.w, fb.w, acc, 0, 0, 0);
+    }
+  }
+  lds_barrier();   // every wave's staging reads are done: sred may overwrite them
+  // Accumulator r of lane l is entry (4 (l / 16) + r, l mod 16).
+  if (i < KP) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.sred[wave][4 * kq + r][i] = acc[r];
+  }
+  lds_barrier();
+  for (int p = tid; p < NPAIR; p += TT) {
+    const int a = pair_a(KP, p), b = pair_b(KP, p);
+    double s1 = 0.0, s2 = 0.0;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      s1 = s1 + static_cast<double>(sm.sred[w][a][b]);
+      s2 = s2 + static_cast<double>(sm.sred[w][KP + a][b]);
+    }
+    out[p] = s1;
+    if (two) out2[p] = s2;
+  }
+}
+
 // Energies of the stored values v (per position, per row) into cache c for slice s.
 template <int KP>
 __device__ __forceinline__ void energies_to_cache(const float (&v)[KP][TS<KP>::VEC], const MatDesc& d, int s,
@@ -438,7 +522,7 @@ __global__ __launch_bounds__(TT) void k_thin_energy(StepArgs args, const Tile* _
 // Pass A of a slice.  On return y holds M_t (stored), g the gradient,
 // dloc and sm.dglob the Dimuon factors (also written to the workspace for
 // pass B).  TA: accumulation type of the per-thread Gram sums.
-template <int KP, bool TALL, typename TA>
+template <int KP, bool TALL, typename TA, bool MFG>
 __device__ __forceinline__ void pass_a_core(const StepArgs& args, const MatDesc& d, int s, int parity,
                                             ThinSmem<KP>& sm, bool full, float (&y)[KP][TS<KP>::VEC],
                                             float (&g)[KP][TS<KP>::VEC], float (&dloc)[TS<KP>::VEC]) {
@@ -522,27 +606,31 @@ __device__ __forceinline__ void pass_a_core(const StepArgs& args, const MatDesc&
     constexpr int GP = gram_group<KP, TA>(), NG = (NPAIR + GP - 1) / GP;
     MUON_GLOBAL double* tg = gmem(reinterpret_cast<double*>(args.ws + d.tg_off)) + static_cast<int64_t>(s) * NPAIR;
     MUON_GLOBAL double* tg2 = gmem(reinterpret_cast<double*>(args.ws + d.tg2_off)) + static_cast<int64_t>(s) * NPAIR;
-    gram_slice<TA, KP, 0, NG>(v, dloc, dimuon, tg, tg2, sm);
+    if constexpr (MFG) gram_slice_mfma<KP>(v, dloc, dimuon, tg, tg2, sm);
+    else gram_slice<TA, KP, 0, NG>(v, dloc, dimuon, tg, tg2, sm);
   }
 }
 
-// The orthogonaliser's precision sets the Gram's: float32 per-thread sums
-// when the Newton-Schulz products are bf16, float64 in fp32 mode.
-template <int KP, bool TALL, typename TA>
+// The orthogonaliser's precision sets the Gram's: float32 sums in bf16 mode
+// (on the matrix cores for Gram sides 8 and 16), float64 per-thread sums in
+// fp32 mode.
+template <int KP, bool TALL, typename TA, bool MFG>
 __device__ __forceinline__ void pass_a_body(const StepArgs& args, const MatDesc& d, int s, int parity,
                                             ThinSmem<KP>& sm) {
   constexpr int VEC = TS<KP>::VEC;
   float y[KP][VEC], g[KP][VEC], dloc[VEC];
-  pass_a_core<KP, TALL, TA>(args, d, s, parity, sm, slice_full<KP, TALL>(d.k, d.N, d.n, s), y, g, dloc);
+  pass_a_core<KP, TALL, TA, MFG>(args, d, s, parity, sm, slice_full<KP, TALL>(d.k, d.N, d.n, s), y, g, dloc);
 }
 
-template <int KP, typename TA>
+// MFG: the slice's Gram on the matrix cores (bf16 mode, Gram side 8).
+template <int KP, typename TA, bool MFG>
 __global__ __launch_bounds__(TT, 4) void k_thin_a(StepArgs args, const Tile* __restrict__ tiles, int parity) {
+  static_assert(!MFG || (sizeof(TA) == 4 && gram_on_mfma<KP>()), "matrix-core Gram: bf16 mode, Gram side 8");
   __shared__ ThinSmem<KP> sm;
   const Tile t = tiles[blockIdx.x];
   const MatDesc& d = args.desc[t.mat];
-  if (d.tall) pass_a_body<KP, true, TA>(args, d, t.ti, parity, sm);
-  else pass_a_body<KP, false, TA>(args, d, t.ti, parity, sm);
+  if (d.tall) pass_a_body<KP, true, TA, MFG>(args, d, t.ti, parity, sm);
+  else pass_a_body<KP, false, TA, MFG>(args, d, t.ti, parity, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -879,17 +967,24 @@ hipError_t launch_thin_energy(const StepArgs& a, const Tile* tiles, int n, int k
 template <typename TA>
 hipError_t launch_thin_a_t(const StepArgs& a, const Tile* tiles, int n, int kp, int parity, hipStream_t s) {
   switch (kp) {
-    case 1: hipLaunchKernelGGL((k_thin_a<1, TA>), dim3(n), dim3(TT), 0, s, a, tiles, parity); break;
-    case 2: hipLaunchKernelGGL((k_thin_a<2, TA>), dim3(n), dim3(TT), 0, s, a, tiles, parity); break;
-    case 4: hipLaunchKernelGGL((k_thin_a<4, TA>), dim3(n), dim3(TT), 0, s, a, tiles, parity); break;
-    case 8: hipLaunchKernelGGL((k_thin_a<8, TA>), dim3(n), dim3(TT), 0, s, a, tiles, parity); break;
-    case 16: hipLaunchKernelGGL((k_thin_a<16, TA>), dim3(n), dim3(TT), 0, s, a, tiles, parity); break;
-    case 32: hipLaunchKernelGGL((k_thin_a<32, TA>), dim3(n), dim3(TT), 0, s, a, tiles, parity); break;
+    case 1: hipLaunchKernelGGL((k_thin_a<1, TA, false>), dim3(n), dim3(TT), 0, s, a, tiles, parity); break;
+    case 2: hipLaunchKernelGGL((k_thin_a<2, TA, false>), dim3(n), dim3(TT), 0, s, a, tiles, parity); break;
+    case 4: hipLaunchKernelGGL((k_thin_a<4, TA, false>), dim3(n), dim3(TT), 0, s, a, tiles, parity); break;
+    case 8:
+      // All slices in one round of workgroups: the pass is latency-bound and
+      // the matrix-core Gram is shorter.  More slices: throughput-bound, and
+      // the per-thread sums cost the matrix pipe nothing.
+      if (std::is_same<TA, float>::value && n <= kThinMfmaGramSlices)
+        hipLaunchKernelGGL((k_thin_a<8, float, true>), dim3(n), dim3(TT), 0, s, a, tiles, parity);
+      else
+        hipLaunchKernelGGL((k_thin_a<8, TA, false>), dim3(n), dim3(TT), 0, s, a, tiles, parity);
+      break;
+    case 16: hipLaunchKernelGGL((k_thin_a<16, TA, false>), dim3(n), dim3(TT), 0, s, a, tiles, parity); break;
+    case 32: hipLaunchKernelGGL((k_thin_a<32, TA, false>), dim3(n), dim3(TT), 0, s, a, tiles, parity); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
-
 hipError_t launch_thin_a(const StepArgs& a, const Tile* tiles, int n, int kp, int parity, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (a.ns_dt == DT_BF16) return launch_thin_a_t<float>(a, tiles, n, kp, parity, s);

@@ -87,10 +87,13 @@ def test_thin_ragged_shapes(shape, variant):
         run_case(wl, variant, cfg_of(wl))
 
 
+@pytest.mark.parametrize("pairs,seed", [(150, 3), (64, 0)])
 @pytest.mark.parametrize("variant", ["muon", "dimuon"])
-def test_thin_large_batch(variant):
-    # 150 LoRA pairs: 2400 slices, more workgroups than the GPU holds at once.
-    wl = W.lora_batch(pairs=150, rank=8, d=4096, seed=3)
+def test_thin_large_batch(variant, pairs, seed):
+    # 150 LoRA pairs: 2400 slices, more workgroups than the GPU holds at once;
+    # 64 pairs: the full LoRA batch.  Every matrix is checked: the outlier
+    # columns make some of them ill-conditioned, and those amplify Gram errors.
+    wl = W.lora_batch(pairs=pairs, rank=8, d=4096, seed=seed)
     cfg = cfg_of(wl)
     params = [D.Param(w=m.w.cuda(), g=m.g.cuda(), mom=m.m_prev.cuda()) for m in wl.mats]
     fn = D.dimuon_step if variant == "dimuon" else D.muon_step
@@ -98,7 +101,7 @@ def test_thin_large_batch(variant):
     kinds = launch_kinds(lambda: fn(params, cfg))
     assert kinds.count("thin_a") == 1 and kinds.count("thin_b") == 1, kinds
     del params
-    run_case(wl, variant, cfg, indices=[0, 1, wl.count // 2, wl.count - 1])
+    run_case(wl, variant, cfg)
 
 
 # ---------------------------------------------------------------------------
