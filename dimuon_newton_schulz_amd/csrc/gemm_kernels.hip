@@ -14,7 +14,7 @@
 // bf16 path: a BM x BN workgroup tile (BM, BN in {128, 256}), four wave64 in
 // a 2 x 2 grid, each wave owning (BM/2) x (BN/2) as 32 x 32 blocks of
 // v_mfma_f32_32x32x16_bf16.  Operands go from global memory straight into a
-// ring of LDS stages of 32 k-values (global_load_lds_dwordx4, no register
+// ring of LDS stages of 64 k-values (global_load_lds_dwordx4, no register
 // staging); all stages but the one being multiplied are in flight (the loop
 // is pipelined so that LDS fragment reads are covered by MFMAs).  A 256 x 256
 // tile reads half as many LDS bytes per MFMA as a 128 x 128 one and needs half
@@ -33,25 +33,27 @@ namespace muon {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int LBK = 32;   // k per pipeline stage
+constexpr int LBK = 64;        // k per pipeline stage: whole 128-byte lines of each operand row
+constexpr int NQ = LBK / 16;   // MFMA k-steps per stage
 
-// Ring depth: the main loop is bound by the operand bytes each CU keeps in
-// flight, and the LDS ring is the only buffer, so the ring takes all the LDS
-// a workgroup may have: 160 KB for 256 x 256 (five stages, four in flight),
-// 144 KB for 128 x 256, and 80 KB for 128 x 128 (two workgroups per CU).
+// The ring takes all the LDS a workgroup may have: 160 KB for 256 x 256 (two
+// stages of 64 KB), 144 KB for 128 x 256 (three of 48 KB), 80 KB for
+// 128 x 128 (two of 32 KB; two workgroups per CU).  Whole-line stages fetch
+// faster than half-line ones (each row's 128 bytes arrive as one request).
 template <int BM, int BN>
 struct GemmT {
   static constexpr int MS = BM / 64, NS = BN / 64;   // 32 x 32 blocks per wave
-  static constexpr int LA = BM / 64, LB = BN / 64;   // 16-byte LDS loads per thread and stage
+  static constexpr int LA = BM / 32, LB = BN / 32;   // 16-byte LDS loads per thread and stage
   static constexpr int LPS = LA + LB;
   static constexpr int STAGE = (BM + BN) * LBK;      // bf16 elements per stage: A rows, then B rows
-  static constexpr int NSTG = BM + BN == 384 ? 6 : 5;
+  static constexpr int BUDGET = BM * BN == 16384 ? 81920 : 163840;
+  static constexpr int NSTG = BUDGET / (STAGE * 2);
   static constexpr int SP = BM / 2 + 2;              // epilogue staging row stride (floats)
   union Smem {
     uint16_t buf[NSTG][STAGE];
     float st[BN * SP];                               // half a tile, transposed, fp32
   };
-  static_assert(sizeof(Smem) <= (BM * BN == 16384 ? 81920 : 163840), "LDS budget");
+  static_assert(NSTG >= 2 && sizeof(Smem) <= BUDGET, "LDS budget");
 };
 
 // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous
@@ -68,13 +70,14 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// A stage holds rows of 32 k-values (64 bytes, four 16-byte chunks).  Chunk
-// c of row r sits at chunk slot c ^ ((r >> 2) & 3): the 32 rows a fragment
-// read touches at one logical chunk then spread over all banks.
-__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+// A stage holds rows of 64 k-values (128 bytes, eight 16-byte chunks).
+// Chunk c of row r sits at chunk slot c ^ ((r >> 1) & 7): the 16 rows a
+// phase of a fragment read touches at one logical chunk then fall on 16
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 // Direct global -> LDS loads of stage `st` (k0 = st * LBK) into buffer b.  A
-// wave's load writes 64 consecutive 16-byte LDS chunks (16 rows); each lane
+// wave's load writes 64 consecutive 16-byte LDS chunks (8 rows); each lane
 // fetches the global chunk that belongs in its slot.
 template <int BM, int BN>
 __device__ __forceinline__ void issue_stage(const MUON_GLOBAL uint16_t* P, int64_t ldp, const MUON_GLOBAL uint16_t* Q,
@@ -86,8 +89,8 @@ __device__ __forceinline__ void issue_stage(const MUON_GLOBAL uint16_t* P, int64
   for (int q = 0; q < G::LA + G::LB; ++q) {
     const bool is_a = q < G::LA;
     const int blk = (is_a ? q : q - G::LA) * 4 + wave;
-    const int row = blk * 16 + (lane >> 2);
-    const int lch = (lane & 3) ^ swz(row);
+    const int row = blk * 8 + (lane >> 3);
+    const int lch = (lane & 7) ^ swz(row);
     const MUON_GLOBAL uint16_t* src = is_a ? P + row * ldp + k0 + lch * 8 : Q + row * ldq + k0 + lch * 8;
     uint16_t* dst = buf + (is_a ? 0 : BM * LBK) + blk * 512;
     __builtin_amdgcn_global_load_lds((const MUON_GLOBAL void*)(src), (__attribute__((address_space(3))) void*)(dst),
@@ -108,13 +111,13 @@ __device__ __forceinline__ void wait_groups(int n) {
 }
 
 // acc[s][t] += P[rows wr*BM/2 + s*32 ..][k] * Q[rows wc*BN/2 + t*32 ..][k] over k < K
-// (K a multiple of 4 * LBK).  A stage holds two k-halves of 16; S = NSTG.
-// Iteration kt:
-//   read half 1 of stage kt;  MFMAs of half 0 (read in the previous iteration)
+// (K a multiple of 2 * LBK).  A stage holds NQ k-steps of 16; S = NSTG.
+// Iteration kt, with fragments read one k-step ahead of the MFMAs:
+//   k-steps 1 .. NQ-1 of stage kt: read step q, MFMAs of step q-1
 //   wait for this wave's loads of stage kt+1; barrier
 //   load stage kt+S into stage kt's buffer (every wave has its fragments of
 //   stage kt in registers: LDS reads complete before the barrier)
-//   read half 0 of stage kt+1;  MFMAs of half 1
+//   read step 0 of stage kt+1;  MFMAs of step NQ-1
 // so fragment reads are always covered by MFMAs, and S-1 stages are in
 // flight while one is multiplied.  The first S stages are issued before the
 // loop.
@@ -123,44 +126,48 @@ __device__ __forceinline__ void mma_nt_bf16(const uint16_t* Pg, int64_t ldp, con
                                             int K, typename GemmT<BM, BN>::Smem& sm,
                                             f32x16_t (&acc)[BM / 64][BN / 64]) {
   using G = GemmT<BM, BN>;
-  constexpr int MS = G::MS, NS = G::NS, LPS = G::LPS;
+  constexpr int MS = G::MS, NS = G::NS, LPS = G::LPS, NSTG = G::NSTG;
+  static_assert(NQ % 2 == 0, "fragment sets alternate");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const MUON_GLOBAL uint16_t* P = gmem(Pg);
   const MUON_GLOBAL uint16_t* Q = gmem(Qg);
-  constexpr int NSTG = G::NSTG;
   const int nk = K / LBK;
 #pragma unroll
   for (int st = 0; st < NSTG; ++st)
     if (st < nk) issue_stage<BM, BN>(P, ldp, Q, ldq, st, sm.buf[st]);
   // Fragment addresses (elements within a stage): row (lane & 31) of each
-  // 32-row block, logical chunk 2 kk + (lane >> 5).
-  const int fr = lane & 31, sw = swz(fr);
-  const int ch0 = ((lane >> 5) ^ sw) * 8, ch1 = ((2 + (lane >> 5)) ^ sw) * 8;
+  // 32-row block, logical chunk 2 q + (lane >> 5) for k-step q.  The swizzle
+  // of a row depends on its index mod 16 only, i.e. on lane & 31.
+  const int fr = lane & 31, sw = swz(fr), half = lane >> 5;
   const int a_off = (wr * (BM / 2) + fr) * LBK, b_off = BM * LBK + (wc * (BN / 2) + fr) * LBK;
-  bf16x8_t fa0[MS], fb0[NS], fa1[MS], fb1[NS];
-  auto read_half = [&](const uint16_t* buf, int ch, bf16x8_t (&fa)[MS], bf16x8_t (&fb)[NS]) {
+  bf16x8_t fa[2][MS], fb[2][NS];
+  auto read_step = [&](const uint16_t* buf, int q, bf16x8_t (&ra)[MS], bf16x8_t (&rb)[NS]) {
+    const int ch = ((2 * q + half) ^ sw) * 8;
 #pragma unroll
-    for (int s = 0; s < MS; ++s) fa[s] = *reinterpret_cast<const bf16x8_t*>(buf + a_off + s * 32 * LBK + ch);
+    for (int s = 0; s < MS; ++s) ra[s] = *reinterpret_cast<const bf16x8_t*>(buf + a_off + s * 32 * LBK + ch);
 #pragma unroll
-    for (int t = 0; t < NS; ++t) fb[t] = *reinterpret_cast<const bf16x8_t*>(buf + b_off + t * 32 * LBK + ch);
+    for (int t = 0; t < NS; ++t) rb[t] = *reinterpret_cast<const bf16x8_t*>(buf + b_off + t * 32 * LBK + ch);
   };
-  auto mfma_half = [&](const bf16x8_t (&fa)[MS], const bf16x8_t (&fb)[NS]) {
+  auto mfma_step = [&](const bf16x8_t (&ra)[MS], const bf16x8_t (&rb)[NS]) {
 #pragma unroll
     for (int s = 0; s < MS; ++s)
 #pragma unroll
       for (int t = 0; t < NS; ++t)
-        acc[s][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s], fb[t], acc[s][t], 0, 0, 0);
+        acc[s][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[s], rb[t], acc[s][t], 0, 0, 0);
   };
   // Stage 0 landed (loads issued after it: stages 1 .. S-1, if any).
   wait_groups<LPS, NSTG - 1>(nk - 1);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  read_half(sm.buf[0], ch0, fa0, fb0);
+  read_step(sm.buf[0], 0, fa[0], fb[0]);
   for (int kt = 0; kt < nk; ++kt) {
     const uint16_t* buf = sm.buf[kt % NSTG];
-    read_half(buf, ch1, fa1, fb1);
-    mfma_half(fa0, fb0);
+#pragma unroll
+    for (int q = 1; q < NQ; ++q) {
+      read_step(buf, q, fa[q & 1], fb[q & 1]);
+      mfma_step(fa[(q - 1) & 1], fb[(q - 1) & 1]);
+    }
     // (The scheduling barriers keep the MFMAs on their side of the wait.)
     __builtin_amdgcn_sched_barrier(0);
     // This wave's reads of stage kt are complete; stage kt+1 has landed.
@@ -170,8 +177,8 @@ __device__ __forceinline__ void mma_nt_bf16(const uint16_t* Pg, int64_t ldp, con
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     __builtin_amdgcn_sched_barrier(0);
     if (kt + NSTG < nk) issue_stage<BM, BN>(P, ldp, Q, ldq, kt + NSTG, sm.buf[kt % NSTG]);
-    if (kt + 1 < nk) read_half(sm.buf[(kt + 1) % NSTG], ch0, fa0, fb0);
-    mfma_half(fa1, fb1);
+    if (kt + 1 < nk) read_step(sm.buf[(kt + 1) % NSTG], 0, fa[0], fb[0]);
+    mfma_step(fa[(NQ - 1) & 1], fb[(NQ - 1) & 1]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
