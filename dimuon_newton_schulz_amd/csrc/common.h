@@ -115,12 +115,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Round-to-nearest-even float -> bfloat16 bits; NaN stays a quiet NaN.
+// Round-to-nearest-even float -> bfloat16 bits (v_cvt_pk_bf16_f32); NaN
+// stays a quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Two floats as packed bfloat16 (a in the low half), one conversion.
+typedef __bf16 bf16x2_pk_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_pk_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float load_elem(const void* p, int64_t idx, int32_t dt) {
@@ -183,8 +188,8 @@ __device__ __forceinline__ void store4_aligned(void* p, int64_t idx, int32_t dt,
     *reinterpret_cast<MUON_GLOBAL float4*>(gmem(static_cast<float*>(p)) + idx) = make_float4(v[0], v[1], v[2], v[3]);
   } else {
     uint2 u;
-    u.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-    u.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+    u.x = pack_bf16x2(v[0], v[1]);
+    u.y = pack_bf16x2(v[2], v[3]);
     *reinterpret_cast<MUON_GLOBAL uint2*>(gmem(static_cast<uint16_t*>(p)) + idx) = u;
   }
 }

@@ -201,10 +201,6 @@ __device__ __forceinline__ int blk_col(int t) {
   return (wave & 1) * (BN / 2) + t * 32 + (lane & 31);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
-}
-
 // Eight consecutive values at element idx: bf16 (16 bytes) or f32 (32 bytes).
 __device__ __forceinline__ void store8(void* p, int64_t idx, int32_t dt, const float (&v)[8]) {
   if (dt == DT_BF16) {

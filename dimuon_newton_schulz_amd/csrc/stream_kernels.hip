@@ -48,10 +48,10 @@ __device__ __forceinline__ void store8(void* p, int32_t dt, int64_t rowoff, int 
       q[1] = make_float4(v[4], v[5], v[6], v[7]);
     } else {
       uint4 u;
-      u.x = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-      u.y = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-      u.z = f32_to_bf16(v[4]) | (static_cast<uint32_t>(f32_to_bf16(v[5])) << 16);
-      u.w = f32_to_bf16(v[6]) | (static_cast<uint32_t>(f32_to_bf16(v[7])) << 16);
+      u.x = pack_bf16x2(v[0], v[1]);
+      u.y = pack_bf16x2(v[2], v[3]);
+      u.z = pack_bf16x2(v[4], v[5]);
+      u.w = pack_bf16x2(v[6], v[7]);
       *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p) + rowoff + col0) = u;
     }
   } else {
@@ -315,10 +315,10 @@ __global__ __launch_bounds__(256) void k_prescale(StepArgs a, const Tile* __rest
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         uint4 u;
-        u.x = f32_to_bf16(v[8 * e + 0]) | (static_cast<uint32_t>(f32_to_bf16(v[8 * e + 1])) << 16);
-        u.y = f32_to_bf16(v[8 * e + 2]) | (static_cast<uint32_t>(f32_to_bf16(v[8 * e + 3])) << 16);
-        u.z = f32_to_bf16(v[8 * e + 4]) | (static_cast<uint32_t>(f32_to_bf16(v[8 * e + 5])) << 16);
-        u.w = f32_to_bf16(v[8 * e + 6]) | (static_cast<uint32_t>(f32_to_bf16(v[8 * e + 7])) << 16);
+        u.x = pack_bf16x2(v[8 * e + 0], v[8 * e + 1]);
+        u.y = pack_bf16x2(v[8 * e + 2], v[8 * e + 3]);
+        u.z = pack_bf16x2(v[8 * e + 4], v[8 * e + 5]);
+        u.w = pack_bf16x2(v[8 * e + 6], v[8 * e + 7]);
         q[e] = u;
       }
     }
@@ -338,10 +338,10 @@ __global__ __launch_bounds__(256) void k_prescale(StepArgs a, const Tile* __rest
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         uint4 u;
-        u.x = f32_to_bf16(v[8 * e + 0]) | (static_cast<uint32_t>(f32_to_bf16(v[8 * e + 1])) << 16);
-        u.y = f32_to_bf16(v[8 * e + 2]) | (static_cast<uint32_t>(f32_to_bf16(v[8 * e + 3])) << 16);
-        u.z = f32_to_bf16(v[8 * e + 4]) | (static_cast<uint32_t>(f32_to_bf16(v[8 * e + 5])) << 16);
-        u.w = f32_to_bf16(v[8 * e + 6]) | (static_cast<uint32_t>(f32_to_bf16(v[8 * e + 7])) << 16);
+        u.x = pack_bf16x2(v[8 * e + 0], v[8 * e + 1]);
+        u.y = pack_bf16x2(v[8 * e + 2], v[8 * e + 3]);
+        u.z = pack_bf16x2(v[8 * e + 4], v[8 * e + 5]);
+        u.w = pack_bf16x2(v[8 * e + 6], v[8 * e + 7]);
         q[e] = u;
       }
     }

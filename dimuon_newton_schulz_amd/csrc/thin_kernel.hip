@@ -101,12 +101,12 @@ __device__ __forceinline__ void vstore(MUON_GLOBAL S* p, const float* v) {
   } else {
     if constexpr (C == 4) {
       uint2 u;
-      u.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-      u.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+      u.x = pack_bf16x2(v[0], v[1]);
+      u.y = pack_bf16x2(v[2], v[3]);
       *reinterpret_cast<MUON_GLOBAL uint2*>(p) = u;
     } else {
       *reinterpret_cast<MUON_GLOBAL uint32_t*>(p) =
-          static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+          pack_bf16x2(v[0], v[1]);
     }
   }
 }
