@@ -322,7 +322,8 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
   for (uint16_t i : p.gen) {
     MatDesc& d = p.desc[i];
     const size_t kn = static_cast<size_t>(d.KP) * d.NP;
-    for (int b = 0; b < 4; ++b) d.x_off[b] = take(kn * es);
+    // X^T copies only for the fp32 products; the bf16 combine reads X itself.
+    for (int b = 0; b < 4; ++b) d.x_off[b] = ((b & 1) && cfg->ns_dtype == MUON_BF16) ? -1 : take(kn * es);
     d.a_off = take(static_cast<size_t>(d.KP) * d.KP * es);
     d.b_off = take(static_cast<size_t>(d.KP) * d.KP * es);
     d.z_off = take(kn * 4);

@@ -31,15 +31,17 @@
 namespace muon {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int LBK = 64;        // k per pipeline stage: whole 128-byte lines of each operand row
 constexpr int NQ = LBK / 16;   // MFMA k-steps per stage
 
-// The ring takes all the LDS a workgroup may have: 160 KB for 256 x 256 (two
-// stages of 64 KB), 144 KB for 128 x 256 (three of 48 KB), 80 KB for
-// 128 x 128 (two of 32 KB; two workgroups per CU).  Whole-line stages fetch
-// faster than half-line ones (each row's 128 bytes arrive as one request).
+// The ring holds two stages of 64 k (128 KB for 256 x 256, 96 KB for
+// 128 x 256, 64 KB for 128 x 128, which runs two workgroups per CU); one is
+// multiplied while the next is in flight.  Whole-line stages fetch faster
+// than half-line ones (each row's 128 bytes arrive as one request), and a
+// deeper ring of shorter stages measured no faster.
 template <int BM, int BN>
 struct GemmT {
   static constexpr int MS = BM / 64, NS = BN / 64;   // 32 x 32 blocks per wave
@@ -47,13 +49,27 @@ struct GemmT {
   static constexpr int LPS = LA + LB;
   static constexpr int STAGE = (BM + BN) * LBK;      // bf16 elements per stage: A rows, then B rows
   static constexpr int BUDGET = BM * BN == 16384 ? 81920 : 163840;
-  static constexpr int NSTG = BUDGET / (STAGE * 2);
   static constexpr int SP = BM / 2 + 2;              // epilogue staging row stride (floats)
-  union Smem {
-    uint16_t buf[NSTG][STAGE];
+  union Smem {                                       // symmetric products
+    uint16_t buf[2][STAGE];
     float st[BN * SP];                               // half a tile, transposed, fp32
   };
-  static_assert(NSTG >= 2 && sizeof(Smem) <= BUDGET, "LDS budget");
+  static_assert(sizeof(Smem) <= BUDGET, "LDS budget");
+};
+
+// The combine's shared memory: its two stages are separate arrays, because
+// the compiler orders a transposing LDS read after pending direct loads
+// unless it can tell their arrays apart.  The epilogue stages in R rounds
+// (R = 4 for 256-row tiles) that alternate between the two arrays, each
+// sized for a stage and for a round.
+template <int BM, int BN>
+struct CombT {
+  using G = GemmT<BM, BN>;
+  static constexpr int R = G::MS >= 4 ? 4 : 2;
+  static constexpr int SPR = BM / R + 2;             // staged row stride (floats)
+  static constexpr int STG = BN * SPR * 2;           // staging of a round, in bf16 elements
+  static constexpr int RB = G::STAGE > STG ? G::STAGE : STG;
+  static_assert(2 * RB * 2 <= G::BUDGET, "LDS budget");
 };
 
 // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous
@@ -76,78 +92,108 @@ __device__ __forceinline__ void wait_vm() {
 // distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
+// A k-major operand (QT: Q[k][n], n contiguous) is staged as LBK rows of BN
+// values; chunk c of k-row r sits at slot c ^ (4 (r & 3)), so that the four
+// k-rows one transposing read touches fall on distinct banks.
+__device__ __forceinline__ int qswz(int row) { return 4 * (row & 3); }
+
 // Direct global -> LDS loads of stage `st` (k0 = st * LBK) into buffer b.  A
-// wave's load writes 64 consecutive 16-byte LDS chunks (8 rows); each lane
-// fetches the global chunk that belongs in its slot.
-template <int BM, int BN>
+// wave's load writes 64 consecutive 16-byte LDS chunks (8 rows of P, or of Q
+// when n-major; 512 / BN k-rows of Q when k-major); each lane fetches the
+// global chunk that belongs in its slot.
+template <int BM, int BN, bool QT>
 __device__ __forceinline__ void issue_stage(const MUON_GLOBAL uint16_t* P, int64_t ldp, const MUON_GLOBAL uint16_t* Q,
                                             int64_t ldq, int st, uint16_t* buf) {
   using G = GemmT<BM, BN>;
+  constexpr int LPR = BN / 8, RPI = 64 / LPR;   // k-major Q: lanes per k-row, k-rows per load
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int k0 = st * LBK;
 #pragma unroll
   for (int q = 0; q < G::LA + G::LB; ++q) {
     const bool is_a = q < G::LA;
     const int blk = (is_a ? q : q - G::LA) * 4 + wave;
-    const int row = blk * 8 + (lane >> 3);
-    const int lch = (lane & 7) ^ swz(row);
-    const MUON_GLOBAL uint16_t* src = is_a ? P + row * ldp + k0 + lch * 8 : Q + row * ldq + k0 + lch * 8;
+    const MUON_GLOBAL uint16_t* src;
+    if (QT && !is_a) {
+      const int r = blk * RPI + lane / LPR;
+      const int c = (lane % LPR) ^ qswz(r);
+      src = Q + (k0 + r) * ldq + c * 8;
+    } else {
+      const int row = blk * 8 + (lane >> 3);
+      const int lch = (lane & 7) ^ swz(row);
+      src = is_a ? P + row * ldp + k0 + lch * 8 : Q + row * ldq + k0 + lch * 8;
+    }
     uint16_t* dst = buf + (is_a ? 0 : BM * LBK) + blk * 512;
     __builtin_amdgcn_global_load_lds((const MUON_GLOBAL void*)(src), (__attribute__((address_space(3))) void*)(dst),
                                      16, 0, 0);
   }
 }
 
-// Waits until at most min(n, G) groups of LPS loads are outstanding (n is
-// uniform across the wave).
-template <int LPS, int G>
-__device__ __forceinline__ void wait_groups(int n) {
-  if constexpr (G == 0) {
-    wait_vm<0>();
-  } else {
-    if (n >= G) wait_vm<G * LPS>();
-    else wait_groups<LPS, G - 1>(n);
-  }
-}
-
-// acc[s][t] += P[rows wr*BM/2 + s*32 ..][k] * Q[rows wc*BN/2 + t*32 ..][k] over k < K
-// (K a multiple of 2 * LBK).  A stage holds NQ k-steps of 16; S = NSTG.
-// Iteration kt, with fragments read one k-step ahead of the MFMAs:
+// acc[s][t] += sum over k < K of P[row wr*BM/2 + s*32 + i][k] * Q(k, col wc*BN/2 + t*32 + j),
+// with Q(k, n) = Q[n][k] (n-major, QT false) or Q[k][n] (k-major, QT true);
+// K is a multiple of 2 * LBK.  A stage holds NQ k-steps of 16; the two
+// stages alternate between buffers b0 and b1 (the loop is unrolled by two,
+// so every access names its buffer).  Per stage kt, with fragments read one
+// k-step ahead of the MFMAs:
 //   k-steps 1 .. NQ-1 of stage kt: read step q, MFMAs of step q-1
 //   wait for this wave's loads of stage kt+1; barrier
-//   load stage kt+S into stage kt's buffer (every wave has its fragments of
+//   load stage kt+2 into stage kt's buffer (every wave has its fragments of
 //   stage kt in registers: LDS reads complete before the barrier)
 //   read step 0 of stage kt+1;  MFMAs of step NQ-1
-// so fragment reads are always covered by MFMAs, and S-1 stages are in
-// flight while one is multiplied.  The first S stages are issued before the
-// loop.
-template <int BM, int BN>
-__device__ __forceinline__ void mma_nt_bf16(const uint16_t* Pg, int64_t ldp, const uint16_t* Qg, int64_t ldq,
-                                            int K, typename GemmT<BM, BN>::Smem& sm,
-                                            f32x16_t (&acc)[BM / 64][BN / 64]) {
+// so fragment reads are always covered by MFMAs and one stage is in flight
+// while the other is multiplied.
+//
+// k-major Q: the B fragment of a k-step (lane l: k = 8 (l / 32) + 0..7,
+// n = l mod 32 of the block) comes from two transposing reads
+// (ds_read_b64_tr_b16): in each 16-lane group, lane i receives element
+// i mod 4 of the 8-byte reads of lanes 4 e + i / 4, e = 0..3, so lane m of the
+// group reads the four n-values 4 (m mod 4) .. + 3 of its 16-column half at
+// k-row 8 (l / 32) + m / 4, and four k-rows further down for the second read.
+template <int BM, int BN, bool QT>
+__device__ __forceinline__ void mma_bf16(const uint16_t* Pg, int64_t ldp, const uint16_t* Qg, int64_t ldq, int K,
+                                         uint16_t* b0, uint16_t* b1, f32x16_t (&acc)[BM / 64][BN / 64]) {
   using G = GemmT<BM, BN>;
-  constexpr int MS = G::MS, NS = G::NS, LPS = G::LPS, NSTG = G::NSTG;
+  constexpr int MS = G::MS, NS = G::NS, LPS = G::LPS;
   static_assert(NQ % 2 == 0, "fragment sets alternate");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const MUON_GLOBAL uint16_t* P = gmem(Pg);
   const MUON_GLOBAL uint16_t* Q = gmem(Qg);
   const int nk = K / LBK;
-#pragma unroll
-  for (int st = 0; st < NSTG; ++st)
-    if (st < nk) issue_stage<BM, BN>(P, ldp, Q, ldq, st, sm.buf[st]);
+  issue_stage<BM, BN, QT>(P, ldp, Q, ldq, 0, b0);
+  issue_stage<BM, BN, QT>(P, ldp, Q, ldq, 1, b1);
   // Fragment addresses (elements within a stage): row (lane & 31) of each
   // 32-row block, logical chunk 2 q + (lane >> 5) for k-step q.  The swizzle
   // of a row depends on its index mod 16 only, i.e. on lane & 31.
   const int fr = lane & 31, sw = swz(fr), half = lane >> 5;
   const int a_off = (wr * (BM / 2) + fr) * LBK, b_off = BM * LBK + (wc * (BN / 2) + fr) * LBK;
+  // k-major Q: the reading lane's k-row and n-column in the stage (block t
+  // adds 32 columns, k-step q 16 rows, the second read 4 rows); the swizzle
+  // of those rows is 4 (m / 4) throughout.
+  const int m16 = lane & 15, g16 = lane >> 4;
+  const int t_row = 8 * (g16 >> 1) + (m16 >> 2);
+  const int t_col = wc * (BN / 2) + 16 * (g16 & 1) + 4 * (m16 & 3);
+  const int t_sw = 4 * (m16 >> 2);
   bf16x8_t fa[2][MS], fb[2][NS];
   auto read_step = [&](const uint16_t* buf, int q, bf16x8_t (&ra)[MS], bf16x8_t (&rb)[NS]) {
     const int ch = ((2 * q + half) ^ sw) * 8;
 #pragma unroll
     for (int s = 0; s < MS; ++s) ra[s] = *reinterpret_cast<const bf16x8_t*>(buf + a_off + s * 32 * LBK + ch);
+    if constexpr (QT) {
+      const uint16_t* qb = buf + BM * LBK + (q * 16 + t_row) * BN;
 #pragma unroll
-    for (int t = 0; t < NS; ++t) rb[t] = *reinterpret_cast<const bf16x8_t*>(buf + b_off + t * 32 * LBK + ch);
+      for (int t = 0; t < NS; ++t) {
+        const int col = t_col + 32 * t;
+        const int at = (((col >> 3) ^ t_sw) << 3) + (col & 7);
+        const i16x4_t lo =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(qb + at));
+        const i16x4_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(qb + 4 * BN + at));
+        rb[t] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NS; ++t) rb[t] = *reinterpret_cast<const bf16x8_t*>(buf + b_off + t * 32 * LBK + ch);
+    }
   };
   auto mfma_step = [&](const bf16x8_t (&ra)[MS], const bf16x8_t (&rb)[NS]) {
 #pragma unroll
@@ -156,31 +202,51 @@ __device__ __forceinline__ void mma_nt_bf16(const uint16_t* Pg, int64_t ldp, con
       for (int t = 0; t < NS; ++t)
         acc[s][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[s], rb[t], acc[s][t], 0, 0, 0);
   };
-  // Stage 0 landed (loads issued after it: stages 1 .. S-1, if any).
-  wait_groups<LPS, NSTG - 1>(nk - 1);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  read_step(sm.buf[0], 0, fa[0], fb[0]);
-  for (int kt = 0; kt < nk; ++kt) {
-    const uint16_t* buf = sm.buf[kt % NSTG];
-#pragma unroll
-    for (int q = 1; q < NQ; ++q) {
-      read_step(buf, q, fa[q & 1], fb[q & 1]);
-      mfma_step(fa[(q - 1) & 1], fb[(q - 1) & 1]);
-    }
+  // The point after which stage kt's buffer may be reloaded: this wave's
+  // reads of it are complete and stage kt+1 has landed; no load is in flight.
+  auto sync = [&]() {
     // (The scheduling barriers keep the MFMAs on their side of the wait.)
     __builtin_amdgcn_sched_barrier(0);
-    // This wave's reads of stage kt are complete; stage kt+1 has landed.
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    wait_groups<LPS, NSTG - 2>(nk - 2 - kt);   // stages issued after kt+1: up to kt+S-1
+    wait_vm<0>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + NSTG < nk) issue_stage<BM, BN>(P, ldp, Q, ldq, kt + NSTG, sm.buf[kt % NSTG]);
-    if (kt + 1 < nk) read_step(sm.buf[(kt + 1) % NSTG], 0, fa[0], fb[0]);
+  };
+  // From sync after stage kt to sync after stage kt+1 (cur holds stage kt,
+  // nxt stage kt+1): load stage kt+2 into cur, read step 0 of stage kt+1,
+  // MFMAs of stage kt's last step, then stage kt+1's other steps.  The loop
+  // is entered and closed at a sync, with no load in flight, so the compiler
+  // keeps track of which buffer the loads in flight write.
+  auto half_step = [&](uint16_t* cur, uint16_t* nxt, int kt) {
+    if (kt + 2 < nk) issue_stage<BM, BN, QT>(P, ldp, Q, ldq, kt + 2, cur);
+    read_step(nxt, 0, fa[0], fb[0]);
     mfma_step(fa[(NQ - 1) & 1], fb[(NQ - 1) & 1]);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 1; q < NQ; ++q) {
+      read_step(nxt, q, fa[q & 1], fb[q & 1]);
+      mfma_step(fa[(q - 1) & 1], fb[(q - 1) & 1]);
+    }
+    sync();
+  };
+  // Stage 0 landed (stage 1's loads were issued after it).
+  wait_vm<LPS>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  read_step(b0, 0, fa[0], fb[0]);
+#pragma unroll
+  for (int q = 1; q < NQ; ++q) {
+    read_step(b0, q, fa[q & 1], fb[q & 1]);
+    mfma_step(fa[(q - 1) & 1], fb[(q - 1) & 1]);
   }
+  sync();
+  int kt = 0;
+  for (; kt + 2 < nk; kt += 2) {
+    half_step(b0, b1, kt);
+    half_step(b1, b0, kt + 1);
+  }
+  half_step(b0, b1, kt);   // stage nk-1 (nk is even)
+  mfma_step(fa[(NQ - 1) & 1], fb[(NQ - 1) & 1]);
 }
 
 // Calls f(integral_constant<int, I>) for I = I0 .. N-1: compile-time block
@@ -227,11 +293,11 @@ __device__ __forceinline__ void unpack8_bf16(const uint4& u, float (&v)[8]) {
   }
 }
 
-// Epilogue through LDS, in two rounds.  In round r every wave stages its
-// accumulator blocks s in [r MS/2, (r+1) MS/2), as fp32 and transposed:
-// st[j][il], where staged row il stands for tile row
-//   i(il) = (il / Q) * BM/2 + r * Q + il % Q,   Q = BM/4
-// (the round's quarter of each wave row).  From each round, every thread
+// Epilogue through LDS, in R rounds.  In round r every wave stages its
+// accumulator blocks s in [r MS/R, (r+1) MS/R), as fp32 and transposed, into
+// stage(r): st[j][il], where staged row il stands for tile row
+//   i(il) = (il / QR) * BM/2 + r * QR + il % QR,   QR = BM / (2R)
+// (the round's share of each wave row).  From each round, every thread
 // produces whole 8-element chunks:
 //   out_t(j, i0, v, aux): v[e] = acc of tile element (i0 + e, j)  (a column
 //                         run; contiguous in the transposed output)
@@ -240,21 +306,22 @@ __device__ __forceinline__ void unpack8_bf16(const uint4& u, float (&v)[8]) {
 // aux_n(i, j0) fetch 8 bf16 operand values per chunk (or nothing); a thread
 // issues all of a round's column-run fetches before staging and all of its
 // row-run fetches right after, so that they are in flight together.  The row
-// stride SP = BM/2 + 2 keeps both the column-run reads (consecutive lanes
-// along il) and the row-run reads (16 lanes along il x 4 along j) free of
-// bank conflicts.
-template <int BM, int BN, typename AT, typename AN, typename FT, typename FN>
-__device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[BM / 64][BN / 64],
-                                                typename GemmT<BM, BN>::Smem& sm, bool do_t, bool do_n,
-                                                AT&& aux_t, AN&& aux_n, FT&& out_t, FN&& out_n) {
+// stride BM/R + 2 keeps both the column-run reads (consecutive lanes along
+// il) and the row-run reads (16 lanes along il x 4 along j) free of bank
+// conflicts.  ALT: consecutive rounds stage into different arrays, so a
+// round needs no barrier before its staging (the previous user of its array
+// finished two rounds earlier, before the last round's barrier).
+template <int BM, int BN, int R, bool ALT, typename SF, typename AT, typename AN, typename FT, typename FN>
+__device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[BM / 64][BN / 64], SF&& stage, bool do_t,
+                                                bool do_n, AT&& aux_t, AN&& aux_n, FT&& out_t, FN&& out_n) {
   using G = GemmT<BM, BN>;
-  constexpr int SP = G::SP, HM = BM / 2, QM = BM / 4, MH = G::MS / 2;
-  constexpr int CPR = HM / 8;                 // column-run chunks per staged row
+  constexpr int HM = BM / 2, QR = BM / (2 * R), RM = BM / R, MR = G::MS / R, SPR = RM + 2;
+  static_assert(G::MS % R == 0, "whole blocks per round");
+  constexpr int CPR = RM / 8;                 // column-run chunks per staged row
   constexpr int CT = BN * CPR / 256;          // column-run chunks per thread and round
-  constexpr int NB = HM / 16;                 // blocks of 16 staged rows (row runs)
-  constexpr int CN = HM * (BN / 8) / 256;     // row-run chunks per thread and round
+  constexpr int NB = RM / 16;                 // blocks of 16 staged rows (row runs)
+  constexpr int CN = RM * (BN / 8) / 256;     // row-run chunks per thread and round
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wr = wave >> 1;
-  float* st = sm.st;
   auto t_pos = [&](int q, int& j, int& il) {
     const int c = tid + 256 * q;
     j = c / CPR;
@@ -266,9 +333,10 @@ __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[BM / 64][B
     il = (r % NB) * 16 + i16;
     j0 = ((r / NB) * 4 + jl) * 8;
   };
-#pragma unroll
-  for (int rd = 0; rd < 2; ++rd) {
-    auto row_of = [&](int il) { return (il / QM) * HM + rd * QM + il % QM; };
+  static_for<0, R>([&](auto rdc) {
+    constexpr int rd = rdc;
+    float* st = stage(rd);
+    auto row_of = [&](int il) { return (il / QR) * HM + rd * QR + il % QR; };
     uint4 xt[CT], xn[CN];
     if (do_t)
       static_for<0, CT>([&](auto q) {
@@ -276,12 +344,14 @@ __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[BM / 64][B
         t_pos(q, j, il);
         xt[q] = aux_t(j, row_of(il));
       });
-    __syncthreads();   // the main loop's stages, or the previous round, are no longer read
-    static_for<0, MH * G::NS * 4>([&](auto q) {
+    // The main loop's stages, or the round that last used this array, are
+    // no longer read.
+    if (rd == 0 || !ALT) __syncthreads();
+    static_for<0, MR * G::NS * 4>([&](auto q) {
       constexpr int sl = q / (G::NS * 4), u = (q / 4) % G::NS, g = q % 4;
-      const int s = rd * MH + sl;
-      const int il = wr * QM + sl * 32 + 8 * g + 4 * (lane >> 5);
-      float* p = st + blk_col<BN>(u) * SP + il;
+      const int s = rd * MR + sl;
+      const int il = wr * QR + sl * 32 + 8 * g + 4 * (lane >> 5);
+      float* p = st + blk_col<BN>(u) * SPR + il;
       *reinterpret_cast<float2*>(p) = make_float2(acc[s][u][4 * g], acc[s][u][4 * g + 1]);
       *reinterpret_cast<float2*>(p + 2) = make_float2(acc[s][u][4 * g + 2], acc[s][u][4 * g + 3]);
     });
@@ -298,7 +368,7 @@ __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[BM / 64][B
       static_for<0, CT>([&](auto q) {
         int j, il;
         t_pos(q, j, il);
-        const float* p = st + j * SP + il;
+        const float* p = st + j * SPR + il;
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
@@ -314,10 +384,10 @@ __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[BM / 64][B
         n_pos(q, il, j0);
         float v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = st[(j0 + e) * SP + il];
+        for (int e = 0; e < 8; ++e) v[e] = st[(j0 + e) * SPR + il];
         out_n(row_of(il), j0, v, xn[q]);
       });
-  }
+  });
 }
 
 __device__ __forceinline__ float block_sum256(float v, float* sh) {
@@ -357,8 +427,8 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(StepArgs a, const Tile* __
     for (int u = 0; u < G::NS; ++u)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[s][u][r] = 0.0f;
-  mma_nt_bf16<BT, BT>(P + static_cast<int64_t>(t.ti) * BT * ld, ld, P + static_cast<int64_t>(t.tj) * BT * ld, ld,
-                      static_cast<int>(ld), sm, acc);
+  mma_bf16<BT, BT, false>(P + static_cast<int64_t>(t.ti) * BT * ld, ld, P + static_cast<int64_t>(t.tj) * BT * ld, ld,
+                          static_cast<int>(ld), sm.buf[0], sm.buf[1], acc);
 
   const float alpha = (kind == 0) ? (first ? a.scal[d.scal_idx].inv_nu2 : 1.0f) : cf.c;
   const uint16_t* E = reinterpret_cast<const uint16_t*>(a.ws + d.a_off);
@@ -395,7 +465,7 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(StepArgs a, const Tile* __
     fin(v, aux, diag_tile ? i - j0 : -1);
     store8(dst, (gi0 + i) * ldo + gj0 + j0, DT_BF16, v);
   };
-  staged_epilogue<BT, BT>(acc, sm, true, t.ti != t.tj, aux_t, aux_n, out_t, out_n);
+  staged_epilogue<BT, BT, 2, false>(acc, [&](int) { return sm.st; }, true, t.ti != t.tj, aux_t, aux_n, out_t, out_n);
 }
 
 // ---------------------------------------------------------------------------
@@ -407,11 +477,14 @@ __global__ __launch_bounds__(256, 1) void k_combine_bf16(StepArgs a, const Tile*
                                                       int src_x, int dst_x, int first, Coeffs cf) {
   constexpr bool last = LAST;
   using G = GemmT<BM, BN>;
-  __shared__ typename G::Smem sm;
+  using C = CombT<BM, BN>;
+  __shared__ __attribute__((aligned(16))) uint16_t ring0[C::RB];
+  __shared__ __attribute__((aligned(16))) uint16_t ring1[C::RB];
   const Tile t = tiles[xcd_remap(blockIdx.x, ntiles)];
   const MatDesc& d = a.desc[t.mat];
   const uint16_t* Bm = reinterpret_cast<const uint16_t*>(a.ws + d.b_off);
-  const uint16_t* XT = reinterpret_cast<const uint16_t*>(a.ws + d.x_off[2 * src_x + 1]);
+  const uint16_t* X = reinterpret_cast<const uint16_t*>(a.ws + d.x_off[2 * src_x]);
+  const int64_t gi0 = static_cast<int64_t>(t.ti) * BM, gj0 = static_cast<int64_t>(t.tj) * BN;
   f32x16_t acc[G::MS][G::NS];
 #pragma unroll
   for (int s = 0; s < G::MS; ++s)
@@ -419,20 +492,17 @@ __global__ __launch_bounds__(256, 1) void k_combine_bf16(StepArgs a, const Tile*
     for (int u = 0; u < G::NS; ++u)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[s][u][r] = 0.0f;
-  if constexpr (!XTERM)
-    mma_nt_bf16<BM, BN>(Bm + static_cast<int64_t>(t.ti) * BM * d.KP, d.KP,
-                        XT + static_cast<int64_t>(t.tj) * BN * d.KP, d.KP, d.KP, sm, acc);
+  // B X, with X read k-major: its rows are the product's k.
+  if constexpr (!XTERM) mma_bf16<BM, BN, true>(Bm + gi0 * d.KP, d.KP, X + gj0, d.NP, d.KP, ring0, ring1, acc);
 
   const float alpha = first ? a.scal[d.scal_idx].inv_nu : 1.0f;
-  const int64_t gi0 = static_cast<int64_t>(t.ti) * BM, gj0 = static_cast<int64_t>(t.tj) * BN;
   const bool partials = LAST && a.dimuon;
-  const uint16_t* X = reinterpret_cast<const uint16_t*>(a.ws + d.x_off[2 * src_x]);
   const MUON_GLOBAL float* dgr = gmem(reinterpret_cast<const float*>(a.ws + (d.tall ? d.dc_off : d.dr_off)));
   const MUON_GLOBAL float* dgc = gmem(reinterpret_cast<const float*>(a.ws + (d.tall ? d.dr_off : d.dc_off)));
-  // X' (row-major, NP) and X'^T (KP) while iterating; on the last iteration Z
-  // (f32) in the caller's orientation: row-major for wide, transposed for tall.
+  // X' (row-major, NP) while iterating; on the last iteration Z (f32) in the
+  // caller's orientation: row-major for wide, transposed for tall.
   void* dst_n = last ? (d.tall ? nullptr : a.ws + d.z_off) : a.ws + d.x_off[2 * dst_x];
-  void* dst_t = last ? (d.tall ? a.ws + d.z_off : nullptr) : a.ws + d.x_off[2 * dst_x + 1];
+  void* dst_t = last && d.tall ? a.ws + d.z_off : nullptr;
   const int32_t odt = last ? DT_F32 : DT_BF16;
   float sz = 0.0f, sp = 0.0f;
   // Dimuon's norm partials: sum of v^2 and of (fr v fc)^2 over the tile, with
@@ -449,9 +519,17 @@ __global__ __launch_bounds__(256, 1) void k_combine_bf16(StepArgs a, const Tile*
     sz = sz + v * v;
     sp = sp + p * p;
   };
-  // X[i][j] = X^T[j][i]: column runs read X^T, row runs read X (XTERM only).
+  // XTERM only: row runs read X, column runs read eight values down a column
+  // of X (zero iterations only).
   auto aux_t = [&](int j, int i0) {
-    return XTERM ? fetch8_bf16(XT, (gj0 + j) * d.KP + gi0 + i0) : make_uint4(0, 0, 0, 0);
+    if constexpr (XTERM) {
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = gmem(X)[(gi0 + i0 + e) * d.NP + gj0 + j];
+      return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    } else {
+      return make_uint4(0, 0, 0, 0);
+    }
   };
   auto aux_n = [&](int i, int j0) {
     return XTERM ? fetch8_bf16(X, (gi0 + i) * d.NP + gj0 + j0) : make_uint4(0, 0, 0, 0);
@@ -484,11 +562,12 @@ __global__ __launch_bounds__(256, 1) void k_combine_bf16(StepArgs a, const Tile*
     }
     store8(dst_n, (gi0 + i) * d.NP + gj0 + j0, odt, v);
   };
-  staged_epilogue<BM, BN>(acc, sm, dst_t != nullptr, dst_n != nullptr, aux_t, aux_n, out_t, out_n);
+  auto stage = [&](int rd) { return reinterpret_cast<float*>(rd & 1 ? ring1 : ring0); };
+  staged_epilogue<BM, BN, C::R, true>(acc, stage, dst_t != nullptr, dst_n != nullptr, aux_t, aux_n, out_t, out_n);
   if (LAST && partials) {
-    // The stage buffers are free once every wave has left the main loop.
+    // The staging arrays are free once every wave has left the epilogue.
     __syncthreads();
-    float* red = reinterpret_cast<float*>(sm.buf[0]);
+    float* red = reinterpret_cast<float*>(ring0);
     sz = block_sum256(sz, red);
     sp = block_sum256(sp, red);
     if (threadIdx.x == 0) {

@@ -293,9 +293,9 @@ __global__ __launch_bounds__(256) void k_prescale(StepArgs a, const Tile* __rest
     for (int e = 0; e < 16; ++e) tileS[r][c0 + e] = round_to(v[e], a.ns_dt);
   }
   __syncthreads();
-  // Write Y (Gram orientation) and Y^T, 16 contiguous elements per thread.
+  // Write Y (Gram orientation) and, for the fp32 products, Y^T; 16
+  // contiguous elements per thread.
   char* ybase = a.ws + d.x_off[0];
-  char* ytbase = a.ws + d.x_off[1];
   const int r = tid >> 2, c0 = (tid & 3) * 16;
   float ssq = 0.0f;
   {
@@ -323,28 +323,15 @@ __global__ __launch_bounds__(256) void k_prescale(StepArgs a, const Tile* __rest
       }
     }
   }
-  {
+  if (a.ns_dt == DT_F32) {
     // Y^T[gb0 + r][ga0 + c0 + e] = Y[ga0 + c0 + e][gb0 + r]
     float v[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) v[e] = d.tall ? tileS[r][c0 + e] : tileS[c0 + e][r];
     const int64_t off = static_cast<int64_t>(gb0 + r) * d.KP + ga0 + c0;
-    if (a.ns_dt == DT_F32) {
-      float4* q = reinterpret_cast<float4*>(reinterpret_cast<float*>(ytbase) + off);
+    float4* q = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.ws + d.x_off[1]) + off);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) q[e] = make_float4(v[4 * e], v[4 * e + 1], v[4 * e + 2], v[4 * e + 3]);
-    } else {
-      uint4* q = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(ytbase) + off);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        uint4 u;
-        u.x = pack_bf16x2(v[8 * e + 0], v[8 * e + 1]);
-        u.y = pack_bf16x2(v[8 * e + 2], v[8 * e + 3]);
-        u.z = pack_bf16x2(v[8 * e + 4], v[8 * e + 5]);
-        u.w = pack_bf16x2(v[8 * e + 6], v[8 * e + 7]);
-        q[e] = u;
-      }
-    }
+    for (int e = 0; e < 4; ++e) q[e] = make_float4(v[4 * e], v[4 * e + 1], v[4 * e + 2], v[4 * e + 3]);
   }
   ssq = wave_tree_sum(ssq);
   if ((tid & 63) == 0) red[tid >> 6] = ssq;
