@@ -233,6 +233,33 @@ void plan_gemm_tiles(Plan& p, bool bf16) {
         d.n_pz = (d.KP / bm) * (d.NP / bn);
       }
     }
+    // Symmetric products: a last round of big tiles that fills at most half
+    // the CUs goes to the 128 x 128 list instead (four tiles per big one,
+    // three for a diagonal one; two workgroups per CU).
+    if (kind == 0 && big) {
+      const auto bi = at.find({256, 256});
+      if (bi != at.end()) {
+        const size_t n = lists[bi->second].tiles.size(), r = n % kCUs;
+        if (n > static_cast<size_t>(kCUs) && r > 0 && r <= static_cast<size_t>(kCUs / 2)) {
+          auto si = at.find({128, 128});
+          if (si == at.end()) {
+            si = at.emplace(std::make_pair(128, 128), lists.size()).first;
+            lists.push_back({128, 128, {}, 0});
+          }
+          std::vector<Tile>& bt = lists[bi->second].tiles;
+          std::vector<Tile>& st = lists[si->second].tiles;
+          for (size_t q = n - r; q < n; ++q) {
+            const Tile t = bt[q];
+            for (int ra = 0; ra < 2; ++ra)
+              for (int cb = 0; cb < 2; ++cb) {
+                const int ti = 2 * t.ti + ra, tj = 2 * t.tj + cb;
+                if (ti <= tj) st.push_back({t.mat, static_cast<uint16_t>(ti), static_cast<uint16_t>(tj), 0});
+              }
+          }
+          bt.resize(n - r);
+        }
+      }
+    }
   }
 }
 

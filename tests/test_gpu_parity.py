@@ -134,6 +134,22 @@ def test_square_spectrum_scaled(variant):
     run_case(wl, variant, cfg_of(wl))
 
 
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
+def test_symmetric_tail_tiles(variant):
+    # 8 x 2048^2: 288 upper 256-tiles, one full round on 256 CUs and a tail
+    # of 32, which the planner runs as 128 x 128 tiles in a second launch of
+    # each symmetric product.  The tail belongs to the last matrix.
+    wl = W.square_batch(count=8, n=2048, seed=9, variant=variant)
+    cfg = cfg_of(wl)
+    params = [D.Param(w=m.w.cuda(), g=m.g.cuda(), mom=m.m_prev.cuda()) for m in wl.mats]
+    fn = D.dimuon_step if variant == "dimuon" else D.muon_step
+    announce(f"{wl.name} {variant}: launch kinds")
+    kinds = launch_kinds(lambda: fn(params, cfg))
+    assert kinds.count("gram") == 2 * cfg.ns_steps and kinds.count("poly") == 2 * cfg.ns_steps, kinds
+    del params
+    run_case(wl, variant, cfg, indices=[0, wl.count - 1])
+
+
 def test_moe_scaled_zero_rows():
     wl = W.moe_experts(experts=2, d_model=384, d_ff=264, seed=7)
     gpu, _ = run_case(wl, "dimuon", cfg_of(wl))
