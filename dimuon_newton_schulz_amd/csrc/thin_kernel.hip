@@ -795,21 +795,26 @@ __device__ __forceinline__ void pass_b_tail(const StepArgs& args, const MatDesc&
   }
   lds_barrier();
 
+  // O = post D_g Z D_l with Z = (Q / nu) Y and Y = D_g V D_l (V = M_t, or
+  // G + mu M_t with Nesterov), i.e. O = (post D_g (Q / nu) D_g) V D_l^2: the
+  // k x k factor is scaled once here and each element takes one product.
+  // (Published to the workgroup by the energies' barriers; without Dimuon
+  // the factor is Q / nu itself.)
+  if (dimuon)
+    for (int e = tid; e < KP * KP; e += TT) {
+      const int a = e / KP, b = e % KP;
+      sm.sQf[e] = sm.post * (sm.dglob[a] * (sm.sQf[e] * sm.dglob[b]));
+    }
+
   // ---- energies of M_t for the next step's conditioning --------------------
   if (dimuon) energies_to_cache<KP>(y, d, s, l0, cache_of(args, d, parity ^ 1), sm);
 
-  // ---- Y, Z = Qs Y, O, update ------------------------------------------------
+  // ---- V, O = (post D_g Q D_g / nu) V D_l^2, update --------------------------
   if (args.nesterov) {
 #pragma unroll
     for (int a = 0; a < KP; ++a)
 #pragma unroll
       for (int e = 0; e < VEC; ++e) y[a][e] = g[a][e] + args.mu * y[a][e];
-  }
-  if (dimuon) {
-#pragma unroll
-    for (int a = 0; a < KP; ++a)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) y[a][e] = (sm.dglob[a] * y[a][e]) * dloc[e];
   }
   {
     float z[KP][VEC];
@@ -826,12 +831,14 @@ __device__ __forceinline__ void pass_b_tail(const StepArgs& args, const MatDesc&
       // One row of Q live at a time (all rows hoisted would take KP^2 registers).
       if constexpr (KP >= 8) __builtin_amdgcn_sched_barrier(0);
     }
-    const float post = sm.post;
+    float dl2[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) dl2[e] = dloc[e] * dloc[e];
 #pragma unroll
     for (int a = 0; a < KP; ++a)
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        const float ov = dimuon ? post * ((sm.dglob[a] * z[a][e]) * dloc[e]) : z[a][e];
+        const float ov = dimuon ? z[a][e] * dl2[e] : z[a][e];
         y[a][e] = ov;
         const float upd = __builtin_fmaf(d.update_scale, ov, args.weight_decay * w[a][e]);
         w[a][e] = __builtin_fmaf(-args.lr, upd, w[a][e]);
