@@ -136,18 +136,25 @@ __device__ __forceinline__ void slice_load_s(const void* base, int k, int N, int
   constexpr int VEC = TS<KP>::VEC, C = slice_vec<KP, TALL>();
   const MUON_GLOBAL S* p = gmem(static_cast<const S*>(base));
   if (full) {
+    // Uniform slice (and row) bases plus 32-bit lane offsets: one offset
+    // serves every row, and the loads take their base from scalar registers.
+    const int lb = l0 - static_cast<int>(threadIdx.x) * VEC;   // slice start
+    const uint32_t lt = threadIdx.x * VEC;
     if constexpr (!TALL) {
 #pragma unroll
-      for (int a = 0; a < KP; ++a)
+      for (int a = 0; a < KP; ++a) {
+        const MUON_GLOBAL S* row = p + static_cast<int64_t>(a) * n + lb;
 #pragma unroll
-        for (int e0 = 0; e0 < VEC; e0 += C) vload<S, C>(p + gidx<false>(a, l0 + e0, n), &v[a][e0]);
+        for (int e0 = 0; e0 < VEC; e0 += C) vload<S, C>(row + (lt + e0), &v[a][e0]);
+      }
     } else {
+      const MUON_GLOBAL S* sb = p + static_cast<int64_t>(lb) * n;
 #pragma unroll
       for (int e = 0; e < VEC; ++e)
 #pragma unroll
         for (int a0 = 0; a0 < KP; a0 += C) {
           float t[C];
-          vload<S, C>(p + gidx<true>(a0, l0 + e, n), t);
+          vload<S, C>(sb + ((lt + e) * static_cast<uint32_t>(n) + a0), t);
 #pragma unroll
           for (int i = 0; i < C; ++i) v[a0 + i][e] = t[i];
         }
@@ -174,12 +181,17 @@ __device__ __forceinline__ void slice_store_s(void* base, int k, int N, int n, i
   constexpr int VEC = TS<KP>::VEC, C = slice_vec<KP, TALL>();
   MUON_GLOBAL S* p = gmem(static_cast<S*>(base));
   if (full) {
+    const int lb = l0 - static_cast<int>(threadIdx.x) * VEC;   // slice start
+    const uint32_t lt = threadIdx.x * VEC;
     if constexpr (!TALL) {
 #pragma unroll
-      for (int a = 0; a < KP; ++a)
+      for (int a = 0; a < KP; ++a) {
+        MUON_GLOBAL S* row = p + static_cast<int64_t>(a) * n + lb;
 #pragma unroll
-        for (int e0 = 0; e0 < VEC; e0 += C) vstore<S, C>(p + gidx<false>(a, l0 + e0, n), &v[a][e0]);
+        for (int e0 = 0; e0 < VEC; e0 += C) vstore<S, C>(row + (lt + e0), &v[a][e0]);
+      }
     } else {
+      MUON_GLOBAL S* sb = p + static_cast<int64_t>(lb) * n;
 #pragma unroll
       for (int e = 0; e < VEC; ++e)
 #pragma unroll
@@ -187,7 +199,7 @@ __device__ __forceinline__ void slice_store_s(void* base, int k, int N, int n, i
           float t[C];
 #pragma unroll
           for (int i = 0; i < C; ++i) t[i] = v[a0 + i][e];
-          vstore<S, C>(p + gidx<true>(a0, l0 + e, n), t);
+          vstore<S, C>(sb + ((lt + e) * static_cast<uint32_t>(n) + a0), t);
         }
     }
   } else {
