@@ -36,9 +36,9 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 # profiles/k_thin_lora_batch_64x8x4096.md.
 THIN_SOURCES = ("dimuon_newton_schulz_amd/csrc/thin_kernel.hip", "dimuon_newton_schulz_amd/csrc/common.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "d660994c02cfeb5c686590bef981aafcca8c6c2a8ef1008f5e35e906db146492",
-    "k_thin_a": {"fetch_kib": 18190.3, "write_kib": 19013.5},
-    "k_thin_b": {"fetch_kib": 20436.2, "write_kib": 18496.0},
+    "sources_sha256": "63167563f089ea2b08c458a671fa14e40f3278cb634bc8406f2846d0f9b0ae92",
+    "k_thin_a": {"fetch_kib": 18168.8, "write_kib": 19012.6},
+    "k_thin_b": {"fetch_kib": 20423.7, "write_kib": 18496.1},
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
