@@ -200,7 +200,6 @@ def roofline_for(wl, cfg, per_kind, work, steps):
     kind = max(per_kind, key=lambda k: per_kind[k][0])
     tot_ms, launches = per_kind[kind]
     avg_ms = tot_ms / launches
-    per_launch_iters = 1
     if kind in ("thin_a", "thin_b"):
         nbytes = work[kind + "_bytes"]
         achieved = nbytes / (avg_ms * 1e-3) / 1e9
@@ -215,13 +214,23 @@ def roofline_for(wl, cfg, per_kind, work, steps):
         return kind, {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                       "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": kind,
                       "avg_launch_ms": round(avg_ms, 5)}
+    # A product may take two launches per iteration (a partial last round of
+    # big tiles runs as 128 x 128 tiles): the rate is the product's flops over
+    # its launches' time, per iteration.
     peak = PEAK_TFLOPS[cfg.ns_dtype]
-    achieved = flops / (avg_ms * 1e-3) / 1e12
+    iters = steps * max(cfg.ns_steps, 1)
+    per_iter = launches / iters
+    achieved = flops * iters / (tot_ms * 1e-3) / 1e12
     names = {"combine": "k_combine_bf16", "gram": "k_syrk_bf16", "poly": "k_syrk_bf16"}
-    return kind, {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                  "frac": round(achieved / peak, 4), "traffic": None,
-                  "kernel": names[kind] if cfg.ns_dtype == "bf16" else names[kind].replace("bf16", "f32"),
-                  "avg_launch_ms": round(avg_ms, 5), "flops_per_launch": flops}
+    out = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+           "frac": round(achieved / peak, 4), "traffic": None,
+           "kernel": names[kind] if cfg.ns_dtype == "bf16" else names[kind].replace("bf16", "f32"),
+           "avg_launch_ms": round(avg_ms, 5), "launches_per_iteration": round(per_iter, 3)}
+    if per_iter == 1:
+        out["flops_per_launch"] = flops
+    else:
+        out["flops_per_iteration"] = flops
+    return kind, out
 
 
 def host_sample(name, variant):

@@ -230,34 +230,37 @@ void plan_gemm_tiles(Plan& p, bool bf16) {
         add_tiles(lists[it->second].tiles, i, d.KP / bm, d.KP / bm, true);
       } else {
         add_tiles(lists[it->second].tiles, i, d.KP / bm, d.NP / bn, false);
-        d.n_pz = (d.KP / bm) * (d.NP / bn);
+        d.n_pz = (d.KP / 128) * (d.NP / 128);
       }
     }
-    // Symmetric products: a last round of big tiles that fills at most half
-    // the CUs goes to the 128 x 128 list instead (four tiles per big one,
-    // three for a diagonal one; two workgroups per CU).
-    if (kind == 0 && big) {
-      const auto bi = at.find({256, 256});
-      if (bi != at.end()) {
+    // A last round of big tiles that fills at most half the CUs goes to the
+    // 128 x 128 list instead (two workgroups per CU): each big tile becomes
+    // its 128 x 128 sub-tiles (for a symmetric product only those on or
+    // above the diagonal).
+    if (big) {
+      const std::vector<std::pair<int, int>> bigs = {{256, 256}, {128, 256}, {256, 128}};
+      for (const auto& key : bigs) {
+        const auto bi = at.find(key);
+        if (bi == at.end()) continue;
         const size_t n = lists[bi->second].tiles.size(), r = n % kCUs;
-        if (n > static_cast<size_t>(kCUs) && r > 0 && r <= static_cast<size_t>(kCUs / 2)) {
-          auto si = at.find({128, 128});
-          if (si == at.end()) {
-            si = at.emplace(std::make_pair(128, 128), lists.size()).first;
-            lists.push_back({128, 128, {}, 0});
-          }
-          std::vector<Tile>& bt = lists[bi->second].tiles;
-          std::vector<Tile>& st = lists[si->second].tiles;
-          for (size_t q = n - r; q < n; ++q) {
-            const Tile t = bt[q];
-            for (int ra = 0; ra < 2; ++ra)
-              for (int cb = 0; cb < 2; ++cb) {
-                const int ti = 2 * t.ti + ra, tj = 2 * t.tj + cb;
-                if (ti <= tj) st.push_back({t.mat, static_cast<uint16_t>(ti), static_cast<uint16_t>(tj), 0});
-              }
-          }
-          bt.resize(n - r);
+        if (n <= static_cast<size_t>(kCUs) || r == 0 || r > static_cast<size_t>(kCUs / 2)) continue;
+        auto si = at.find({128, 128});
+        if (si == at.end()) {
+          si = at.emplace(std::make_pair(128, 128), lists.size()).first;
+          lists.push_back({128, 128, {}, 0});
         }
+        std::vector<Tile>& bt = lists[bi->second].tiles;
+        std::vector<Tile>& st = lists[si->second].tiles;
+        const int fm = key.first / 128, fn = key.second / 128;
+        for (size_t q = n - r; q < n; ++q) {
+          const Tile t = bt[q];
+          for (int ra = 0; ra < fm; ++ra)
+            for (int cb = 0; cb < fn; ++cb) {
+              const int ti = fm * t.ti + ra, tj = fn * t.tj + cb;
+              if (kind == 1 || ti <= tj) st.push_back({t.mat, static_cast<uint16_t>(ti), static_cast<uint16_t>(tj), 0});
+            }
+        }
+        bt.resize(n - r);
       }
     }
   }

@@ -50,7 +50,7 @@ struct alignas(16) MatDesc {
   int64_t pr_off;         // row-energy partials [ncb][m] f32
   int64_t pc_off;         // column-energy partials [nrb][n] f32
   int64_t pn_off;         // ||Y||^2 partials, one per prescale tile, f32
-  int64_t pz_off;         // (||Z||^2, ||P||^2) partials, one pair per combine tile, f32
+  int64_t pz_off;         // (||Z||^2, ||P||^2) partials, one pair per 128 x 128 sub-tile of the combine, f32
   int32_t ncb, nrb;       // number of 512-column / 32-row energy blocks
   int32_t n_pn, n_pz;     // partial counts
   int32_t scal_idx;       // index into the per-matrix scalar array

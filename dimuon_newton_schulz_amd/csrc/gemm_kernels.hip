@@ -570,11 +570,14 @@ __global__ __launch_bounds__(256, 1) void k_combine_bf16(StepArgs a, const Tile*
     float* red = reinterpret_cast<float*>(ring0);
     sz = block_sum256(sz, red);
     sp = block_sum256(sp, red);
-    if (threadIdx.x == 0) {
+    // One pair per 128 x 128 sub-tile (a matrix's tiles may mix sizes): the
+    // tile's sums go to its first sub-tile, zeros to the others.
+    if (threadIdx.x < (BM / 128) * (BN / 128)) {
       float* pz = reinterpret_cast<float*>(a.ws + d.pz_off);
-      const int idx = t.ti * (d.NP / BN) + t.tj;
-      pz[2 * idx] = sz;
-      pz[2 * idx + 1] = sp;
+      const int sa = threadIdx.x / (BN / 128), sb = threadIdx.x % (BN / 128);
+      const int idx = (t.ti * (BM / 128) + sa) * (d.NP / 128) + t.tj * (BN / 128) + sb;
+      pz[2 * idx] = threadIdx.x == 0 ? sz : 0.0f;
+      pz[2 * idx + 1] = threadIdx.x == 0 ? sp : 0.0f;
     }
   }
 }

@@ -150,6 +150,23 @@ def test_symmetric_tail_tiles(variant):
     run_case(wl, variant, cfg, indices=[0, wl.count - 1])
 
 
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
+def test_combine_tail_tiles(variant):
+    # 9 x (256 x 7936): 279 combine tiles of 256 x 256, one full round and a
+    # tail of 23 that the planner runs as 128 x 128 tiles in a second launch.
+    # The last matrix mixes both sizes, so its Dimuon norm partials come from
+    # both launches.
+    wl = W.random_batch([(256, 7936)] * 9, dtype="bf16", ns_dtype="bf16", seed=10, variant=variant)
+    cfg = cfg_of(wl)
+    params = [D.Param(w=m.w.cuda(), g=m.g.cuda(), mom=m.m_prev.cuda()) for m in wl.mats]
+    fn = D.dimuon_step if variant == "dimuon" else D.muon_step
+    announce(f"{wl.name} {variant}: launch kinds")
+    kinds = launch_kinds(lambda: fn(params, cfg))
+    assert kinds.count("combine") == 2 * cfg.ns_steps, kinds
+    del params
+    run_case(wl, variant, cfg, indices=[0, wl.count - 1])
+
+
 def test_moe_scaled_zero_rows():
     wl = W.moe_experts(experts=2, d_model=384, d_ff=264, seed=7)
     gpu, _ = run_case(wl, "dimuon", cfg_of(wl))
