@@ -356,7 +356,7 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
     for (int b = 0; b < 4; ++b) d.x_off[b] = ((b & 1) && cfg->ns_dtype == MUON_BF16) ? -1 : take(kn * es);
     d.a_off = take(static_cast<size_t>(d.KP) * d.KP * es);
     d.b_off = take(static_cast<size_t>(d.KP) * d.KP * es);
-    d.z_off = take(kn * 4);
+    d.z_off = take(kn * es);
     if (cfg->nesterov) d.v_off = take(static_cast<size_t>(d.m) * d.n * 4);
     d.dr_off = take(static_cast<size_t>(round_up(d.m, kPad)) * 4);
     d.dc_off = take(static_cast<size_t>(round_up(d.n, kPad)) * 4);

@@ -41,7 +41,7 @@ struct alignas(16) MatDesc {
   int64_t x_off[4];       // X (KP x NP) and X^T (NP x KP, fp32 mode only), ping (0,1) and pong (2,3), ns dtype
   int64_t a_off;          // A = X X^T, KP x KP, ns dtype
   int64_t b_off;          // B = bA + c A A, KP x KP, ns dtype
-  int64_t z_off;          // Z (last iterate), KP x NP, f32
+  int64_t z_off;          // Z (last iterate), KP x NP (transposed for tall), ns dtype
   int64_t v_off;          // Nesterov input, m x n f32 (or -1)
   int64_t dr_off;         // row factors, round_up(m, kPad) f32 (zero beyond m)
   int64_t dc_off;         // column factors, round_up(n, kPad) f32 (zero beyond n)

@@ -499,11 +499,12 @@ __global__ __launch_bounds__(256, 1) void k_combine_bf16(StepArgs a, const Tile*
   const bool partials = LAST && a.dimuon;
   const MUON_GLOBAL float* dgr = gmem(reinterpret_cast<const float*>(a.ws + (d.tall ? d.dc_off : d.dr_off)));
   const MUON_GLOBAL float* dgc = gmem(reinterpret_cast<const float*>(a.ws + (d.tall ? d.dr_off : d.dc_off)));
-  // X' (row-major, NP) while iterating; on the last iteration Z (f32) in the
+  // X' (row-major, NP) while iterating; on the last iteration Z, bf16 like
+  // every iterate (the norm partials below take the fp32 values), in the
   // caller's orientation: row-major for wide, transposed for tall.
   void* dst_n = last ? (d.tall ? nullptr : a.ws + d.z_off) : a.ws + d.x_off[2 * dst_x];
   void* dst_t = last && d.tall ? a.ws + d.z_off : nullptr;
-  const int32_t odt = last ? DT_F32 : DT_BF16;
+  constexpr int32_t odt = DT_BF16;
   float sz = 0.0f, sp = 0.0f;
   // Dimuon's norm partials: sum of v^2 and of (fr v fc)^2 over the tile, with
   // fr, fc the factors of the Gram orientation's rows and columns (the factor

@@ -423,8 +423,7 @@ __global__ __launch_bounds__(256) void k_update(StepArgs a, const Tile* __restri
   const int r = tid >> 2, c0 = (tid & 3) * 16;
   const int row = t.ti * 64 + r;
   if (row >= m) return;
-  const float* z = reinterpret_cast<const float*>(a.ws + d.z_off);
-  const int64_t zld = d.tall ? d.KP : d.NP;
+  const int64_t zld = d.tall ? d.KP : d.NP;   // Z holds the ns dtype
   const MatScal sc = a.scal[d.scal_idx];
   const float* dr = reinterpret_cast<const float*>(a.ws + d.dr_off);
   const float* dc = reinterpret_cast<const float*>(a.ws + d.dc_off);
@@ -435,9 +434,22 @@ __global__ __launch_bounds__(256) void k_update(StepArgs a, const Tile* __restri
     if (col0 >= n) break;
     float w[8], o[8];
     load8(d.w, a.w_dt, off, col0, n, w);
-    const float4* zq = reinterpret_cast<const float4*>(z + static_cast<int64_t>(row) * zld + col0);
-    const float4 z0 = zq[0], z1 = zq[1];
-    const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+    float zv[8];
+    const int64_t zi = static_cast<int64_t>(row) * zld + col0;
+    if (a.ns_dt == DT_F32) {
+      const float4* zq = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.ws + d.z_off) + zi);
+      const float4 z0 = zq[0], z1 = zq[1];
+      zv[0] = z0.x; zv[1] = z0.y; zv[2] = z0.z; zv[3] = z0.w;
+      zv[4] = z1.x; zv[5] = z1.y; zv[6] = z1.z; zv[7] = z1.w;
+    } else {
+      const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.ws + d.z_off) + zi);
+      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        zv[2 * e] = __uint_as_float(w4[e] << 16);
+        zv[2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int col = col0 + e;

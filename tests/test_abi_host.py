@@ -73,9 +73,9 @@ def test_workspace_sizes():
     assert st == 0 and thin < 1 << 20          # the thin path: table, energy caches, Gram partials
     st, big = _ws_bytes(_mats([(4096, 4096)]), 1, c)
     assert st == 0
-    # two X buffers (the bf16 combine reads X itself), A, B (bf16) and Z (f32)
+    # two X buffers (the bf16 combine reads X itself), A, B and Z, all bf16,
     # of 4096^2 at least, and no X^T copies
-    assert 4096 * 4096 * (2 * 2 + 2 * 2 + 4) <= big < 4096 * 4096 * (4 * 2 + 2 * 2 + 4)
+    assert 4096 * 4096 * 2 * (2 + 2 + 1) <= big < 4096 * 4096 * 2 * (4 + 2 + 1)
     c32, _ = _cfg(ns_dtype="f32")
     st, big32 = _ws_bytes(_mats([(4096, 4096)]), 1, c32)
     # fp32: four X buffers (X and X^T, ping and pong), A, B and Z
