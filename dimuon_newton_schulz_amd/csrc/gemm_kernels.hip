@@ -1,29 +1,29 @@
 // Grouped GEMM kernels of the Newton-Schulz iteration.
 //
-// Every product here is "NT": C[i][j] = sum_k P[i][k] Q[j][k], with both
-// operands row-major and K-contiguous.  This works because the workspace
-// keeps each iterate in both layouts, X (k x N) and X^T (N x k):
-//   Gram     A = X X^T        P = X,   Q = X     (K = N)   symmetric
-//   poly     B = a I + b A + c A A   P = A, Q = A   (K = k)   symmetric
-//   combine  X' = B X                P = B, Q = X^T (K = k)
+// The products, C[i][j] = sum_k P[i][k] Q(k, j):
+//   Gram     A = X X^T               P = X, Q(k, j) = X[j][k]   (K = N)  symmetric
+//   poly     B = a I + b A + c A A   P = A, Q(k, j) = A[j][k]   (K = k)  symmetric
+//   combine  X' = B X                P = B, Q(k, j) = X[k][j]   (K = k)
 // (a X + (b A + c A A) X with the a X term folded into B's diagonal, so the
-// combine reads nothing but its two operands.)
-// The symmetric products compute the upper-triangular tiles only and store
-// each such tile and its mirror.  The combine stores X' and X'^T.
+// combine reads nothing but its two operands.)  The symmetric products read
+// both operands K-contiguous ("NT") and compute the upper-triangular tiles
+// only, storing each such tile and its mirror.  The bf16 combine reads X
+// itself k-major (transposing LDS reads), so no X^T is ever written; the fp32
+// kernels at the end of this file keep X^T beside X and stay "NT".
 //
 // bf16 path: a BM x BN workgroup tile (BM, BN in {128, 256}), four wave64 in
 // a 2 x 2 grid, each wave owning (BM/2) x (BN/2) as 32 x 32 blocks of
 // v_mfma_f32_32x32x16_bf16.  Operands go from global memory straight into a
-// ring of LDS stages of 64 k-values (global_load_lds_dwordx4, no register
-// staging); all stages but the one being multiplied are in flight (the loop
+// ring of two LDS stages of 64 k-values (global_load_lds_dwordx4, no register
+// staging); one stage is in flight while the other is multiplied (the loop
 // is pipelined so that LDS fragment reads are covered by MFMAs).  A 256 x 256
 // tile reads half as many LDS bytes per MFMA as a 128 x 128 one and needs half
-// the L2 traffic per flop; with its 160 KB ring and 256 accumulator registers
+// the L2 traffic per flop; with its 128 KB ring and 256 accumulator registers
 // one workgroup runs per CU (two for 128 x 128).
 //
-// The epilogue stages the fp32 accumulators through LDS (transposed, half a
-// tile per round) so that both the row-major and the transposed outputs are
-// written as 16-byte runs.
+// The epilogue stages the fp32 accumulators through LDS (transposed, in
+// rounds) so that the row-major and the transposed outputs are written as
+// 16-byte runs.
 #include <type_traits>
 
 #include "common.h"
