@@ -11,15 +11,15 @@
 // itself k-major (transposing LDS reads), so no X^T is ever written; the fp32
 // kernels at the end of this file keep X^T beside X and stay "NT".
 //
-// bf16 path: a BM x BN workgroup tile (BM, BN in {128, 256}), four wave64 in
-// a 2 x 2 grid, each wave owning (BM/2) x (BN/2) as 32 x 32 blocks of
+// bf16 path: a BM x BN workgroup tile (BM, BN in {128, 256}), wave64s in a
+// 2 x WC grid (eight waves, WC = 4, for the larger tiles; four for 128 x 128),
+// each wave owning (BM/2) x (BN/WC) as 32 x 32 blocks of
 // v_mfma_f32_32x32x16_bf16.  Operands go from global memory straight into a
 // ring of two LDS stages of 64 k-values (global_load_lds_dwordx4, no register
 // staging); one stage is in flight while the other is multiplied (the loop
 // is pipelined so that LDS fragment reads are covered by MFMAs).  A 256 x 256
-// tile reads half as many LDS bytes per MFMA as a 128 x 128 one and needs half
-// the L2 traffic per flop; with its 128 KB ring and 256 accumulator registers
-// one workgroup runs per CU (two for 128 x 128).
+// tile needs half the L2 traffic per flop of a 128 x 128 one; with its 128 KB
+// ring one workgroup runs per CU (two for 128 x 128).
 //
 // The epilogue stages the fp32 accumulators through LDS (transposed, in
 // rounds) so that the row-major and the transposed outputs are written as
@@ -42,10 +42,22 @@ constexpr int NQ = LBK / 16;   // MFMA k-steps per stage
 // multiplied while the next is in flight.  Whole-line stages fetch faster
 // than half-line ones (each row's 128 bytes arrive as one request), and a
 // deeper ring of shorter stages measured no faster.
+// Waves in 2 rows x WC columns.  Tiles of 128 x 256 and larger run eight
+// waves (WC = 4, two per SIMD: one wave's MFMAs cover the other's loads and
+// barrier waits), measured 3-5% faster per step than four; 128 x 128 tiles,
+// two workgroups per CU, keep four (eight measured slower there).
+#ifndef MUON_GEMM_WC_LARGE
+#define MUON_GEMM_WC_LARGE 4
+#endif
+#ifndef MUON_GEMM_WC_SMALL
+#define MUON_GEMM_WC_SMALL 2
+#endif
 template <int BM, int BN>
 struct GemmT {
-  static constexpr int MS = BM / 64, NS = BN / 64;   // 32 x 32 blocks per wave
-  static constexpr int LA = BM / 32, LB = BN / 32;   // 16-byte LDS loads per thread and stage
+  static constexpr int WC = BM * BN >= 32768 ? MUON_GEMM_WC_LARGE : MUON_GEMM_WC_SMALL;
+  static constexpr int NW = 2 * WC, NT = 64 * NW;    // waves, threads
+  static constexpr int MS = BM / 64, NS = BN / (32 * WC);   // 32 x 32 blocks per wave
+  static constexpr int LA = BM * 8 / NT, LB = BN * 8 / NT;  // 16-byte LDS loads per thread and stage
   static constexpr int LPS = LA + LB;
   static constexpr int STAGE = (BM + BN) * LBK;      // bf16 elements per stage: A rows, then B rows
   static constexpr int BUDGET = BM * BN == 16384 ? 81920 : 163840;
@@ -111,7 +123,7 @@ __device__ __forceinline__ void issue_stage(const MUON_GLOBAL uint16_t* P, int64
 #pragma unroll
   for (int q = 0; q < G::LA + G::LB; ++q) {
     const bool is_a = q < G::LA;
-    const int blk = (is_a ? q : q - G::LA) * 4 + wave;
+    const int blk = (is_a ? q : q - G::LA) * G::NW + wave;
     const MUON_GLOBAL uint16_t* src;
     if (QT && !is_a) {
       const int r = blk * RPI + lane / LPR;
@@ -150,12 +162,13 @@ __device__ __forceinline__ void issue_stage(const MUON_GLOBAL uint16_t* P, int64
 // k-row 8 (l / 32) + m / 4, and four k-rows further down for the second read.
 template <int BM, int BN, bool QT>
 __device__ __forceinline__ void mma_bf16(const uint16_t* Pg, int64_t ldp, const uint16_t* Qg, int64_t ldq, int K,
-                                         uint16_t* b0, uint16_t* b1, f32x16_t (&acc)[BM / 64][BN / 64]) {
+                                         uint16_t* b0, uint16_t* b1,
+                                         f32x16_t (&acc)[GemmT<BM, BN>::MS][GemmT<BM, BN>::NS]) {
   using G = GemmT<BM, BN>;
-  constexpr int MS = G::MS, NS = G::NS, LPS = G::LPS;
+  constexpr int MS = G::MS, NS = G::NS, LPS = G::LPS, WN = BN / G::WC;
   static_assert(NQ % 2 == 0, "fragment sets alternate");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
+  const int wr = wave / G::WC, wc = wave % G::WC;
   const MUON_GLOBAL uint16_t* P = gmem(Pg);
   const MUON_GLOBAL uint16_t* Q = gmem(Qg);
   const int nk = K / LBK;
@@ -165,13 +178,13 @@ __device__ __forceinline__ void mma_bf16(const uint16_t* Pg, int64_t ldp, const 
   // 32-row block, logical chunk 2 q + (lane >> 5) for k-step q.  The swizzle
   // of a row depends on its index mod 16 only, i.e. on lane & 31.
   const int fr = lane & 31, sw = swz(fr), half = lane >> 5;
-  const int a_off = (wr * (BM / 2) + fr) * LBK, b_off = BM * LBK + (wc * (BN / 2) + fr) * LBK;
+  const int a_off = (wr * (BM / 2) + fr) * LBK, b_off = BM * LBK + (wc * WN + fr) * LBK;
   // k-major Q: the reading lane's k-row and n-column in the stage (block t
   // adds 32 columns, k-step q 16 rows, the second read 4 rows); the swizzle
   // of those rows is 4 (m / 4) throughout.
   const int m16 = lane & 15, g16 = lane >> 4;
   const int t_row = 8 * (g16 >> 1) + (m16 >> 2);
-  const int t_col = wc * (BN / 2) + 16 * (g16 & 1) + 4 * (m16 & 3);
+  const int t_col = wc * WN + 16 * (g16 & 1) + 4 * (m16 & 3);
   const int t_sw = 4 * (m16 >> 2);
   bf16x8_t fa[2][MS], fb[2][NS];
   auto read_step = [&](const uint16_t* buf, int q, bf16x8_t (&ra)[MS], bf16x8_t (&rb)[NS]) {
@@ -261,10 +274,11 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // Tile-relative column of block t for this lane (rows of a block's
 // accumulator group g are 8g + 4 (lane >> 5) + 0..3).
-template <int BN>
+template <int BM, int BN>
 __device__ __forceinline__ int blk_col(int t) {
+  using G = GemmT<BM, BN>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  return (wave & 1) * (BN / 2) + t * 32 + (lane & 31);
+  return (wave % G::WC) * (BN / G::WC) + t * 32 + (lane & 31);
 }
 
 // Eight consecutive values at element idx: bf16 (16 bytes) or f32 (32 bytes).
@@ -312,23 +326,25 @@ __device__ __forceinline__ void unpack8_bf16(const uint4& u, float (&v)[8]) {
 // round needs no barrier before its staging (the previous user of its array
 // finished two rounds earlier, before the last round's barrier).
 template <int BM, int BN, int R, bool ALT, typename SF, typename AT, typename AN, typename FT, typename FN>
-__device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[BM / 64][BN / 64], SF&& stage, bool do_t,
+__device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[GemmT<BM, BN>::MS][GemmT<BM, BN>::NS],
+                                                SF&& stage, bool do_t,
                                                 bool do_n, AT&& aux_t, AN&& aux_n, FT&& out_t, FN&& out_n) {
   using G = GemmT<BM, BN>;
   constexpr int HM = BM / 2, QR = BM / (2 * R), RM = BM / R, MR = G::MS / R, SPR = RM + 2;
   static_assert(G::MS % R == 0, "whole blocks per round");
   constexpr int CPR = RM / 8;                 // column-run chunks per staged row
-  constexpr int CT = BN * CPR / 256;          // column-run chunks per thread and round
+  constexpr int CT = BN * CPR / G::NT;        // column-run chunks per thread and round
   constexpr int NB = RM / 16;                 // blocks of 16 staged rows (row runs)
-  constexpr int CN = RM * (BN / 8) / 256;     // row-run chunks per thread and round
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wr = wave >> 1;
+  constexpr int CN = RM * (BN / 8) / G::NT;   // row-run chunks per thread and round
+  static_assert(BN * CPR % G::NT == 0 && RM * (BN / 8) % G::NT == 0, "whole chunks per thread");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wr = wave / G::WC;
   auto t_pos = [&](int q, int& j, int& il) {
-    const int c = tid + 256 * q;
+    const int c = tid + G::NT * q;
     j = c / CPR;
     il = (c % CPR) * 8;
   };
   auto n_pos = [&](int q, int& il, int& j0) {
-    const int c = tid + 256 * q;
+    const int c = tid + G::NT * q;
     const int i16 = c & 15, jl = (c >> 4) & 3, r = c >> 6;
     il = (r % NB) * 16 + i16;
     j0 = ((r / NB) * 4 + jl) * 8;
@@ -351,7 +367,7 @@ __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[BM / 64][B
       constexpr int sl = q / (G::NS * 4), u = (q / 4) % G::NS, g = q % 4;
       const int s = rd * MR + sl;
       const int il = wr * QR + sl * 32 + 8 * g + 4 * (lane >> 5);
-      float* p = st + blk_col<BN>(u) * SPR + il;
+      float* p = st + blk_col<BM, BN>(u) * SPR + il;
       *reinterpret_cast<float2*>(p) = make_float2(acc[s][u][4 * g], acc[s][u][4 * g + 1]);
       *reinterpret_cast<float2*>(p + 2) = make_float2(acc[s][u][4 * g + 2], acc[s][u][4 * g + 3]);
     });
@@ -390,12 +406,16 @@ __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[BM / 64][B
   });
 }
 
-__device__ __forceinline__ float block_sum256(float v, float* sh) {
+// Sum over a workgroup of NW waves (4 or 8), the same value in every thread.
+template <int NW>
+__device__ __forceinline__ float block_sum(float v, float* sh) {
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
   v = wave_tree_sum(v);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (lane == 0) sh[wave] = v;
   __syncthreads();
-  const float r = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+  float r = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+  if constexpr (NW == 8) r = r + ((sh[4] + sh[5]) + (sh[6] + sh[7]));
   __syncthreads();
   return r;
 }
@@ -404,7 +424,7 @@ __device__ __forceinline__ float block_sum256(float v, float* sh) {
 // Symmetric products (bf16): kind 0 Gram, kind 1 polynomial.  Square tiles.
 // ---------------------------------------------------------------------------
 template <int BT, int KIND>
-__global__ __launch_bounds__(256, 1) void k_syrk_bf16(StepArgs a, const Tile* __restrict__ tiles, int ntiles,
+__global__ __launch_bounds__((GemmT<BT, BT>::NT), 1) void k_syrk_bf16(StepArgs a, const Tile* __restrict__ tiles, int ntiles,
                                                    int src_x, int first, Coeffs cf) {
   constexpr int kind = KIND;
   using G = GemmT<BT, BT>;
@@ -473,7 +493,7 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(StepArgs a, const Tile* __
 // XTERM (no iterations: Z = alpha a X): the product is skipped and X read.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, bool LAST, bool XTERM>
-__global__ __launch_bounds__(256, 1) void k_combine_bf16(StepArgs a, const Tile* __restrict__ tiles, int ntiles,
+__global__ __launch_bounds__((GemmT<BM, BN>::NT), 1) void k_combine_bf16(StepArgs a, const Tile* __restrict__ tiles, int ntiles,
                                                       int src_x, int dst_x, int first, Coeffs cf) {
   constexpr bool last = LAST;
   using G = GemmT<BM, BN>;
@@ -569,8 +589,8 @@ __global__ __launch_bounds__(256, 1) void k_combine_bf16(StepArgs a, const Tile*
     // The staging arrays are free once every wave has left the epilogue.
     __syncthreads();
     float* red = reinterpret_cast<float*>(ring0);
-    sz = block_sum256(sz, red);
-    sp = block_sum256(sp, red);
+    sz = block_sum<G::NW>(sz, red);
+    sp = block_sum<G::NW>(sp, red);
     // One pair per 128 x 128 sub-tile (a matrix's tiles may mix sizes): the
     // tile's sums go to its first sub-tile, zeros to the others.
     if (threadIdx.x < (BM / 128) * (BN / 128)) {
@@ -724,8 +744,8 @@ __global__ __launch_bounds__(256) void k_combine_f32(StepArgs a, const Tile* __r
     }
   }
   if (partials) {
-    sz = block_sum256(sz, red);
-    sp = block_sum256(sp, red);
+    sz = block_sum<4>(sz, red);
+    sp = block_sum<4>(sp, red);
     if (threadIdx.x == 0) {
       float* pz = reinterpret_cast<float*>(a.ws + d.pz_off);
       const int idx = t.ti * (d.NP / FT) + t.tj;
@@ -747,7 +767,8 @@ hipError_t launch_syrk(const StepArgs& a, const Tile* tiles, int n, int bt, int 
     hipLaunchKernelGGL(k_syrk_f32, dim3(n), dim3(256), 0, s, a, tiles, n, kind, src_x, f, cf);
     return hipGetLastError();
   }
-#define MUON_SYRK(BT, K) hipLaunchKernelGGL((k_syrk_bf16<BT, K>), dim3(n), dim3(256), 0, s, a, tiles, n, src_x, f, cf)
+#define MUON_SYRK(BT, K) \
+  hipLaunchKernelGGL((k_syrk_bf16<BT, K>), dim3(n), dim3(GemmT<BT, BT>::NT), 0, s, a, tiles, n, src_x, f, cf)
   if (bt == 256) {
     if (kind == 0) MUON_SYRK(256, 0); else MUON_SYRK(256, 1);
   } else if (bt == 128) {
@@ -771,13 +792,13 @@ hipError_t launch_combine(const StepArgs& a, const Tile* tiles, int n, int bm, i
 #define MUON_COMB(BM, BN)                                                                                   \
   if (!product) {                                                                                            \
     if (!last) return hipErrorInvalidValue;                                                                  \
-    hipLaunchKernelGGL((k_combine_bf16<BM, BN, true, true>), dim3(n), dim3(256), 0, s, a, tiles, n, src_x,   \
+    hipLaunchKernelGGL((k_combine_bf16<BM, BN, true, true>), dim3(n), dim3(GemmT<BM, BN>::NT), 0, s, a, tiles, n, src_x,   \
                        dst_x, f, cf);                                                                        \
   } else if (last) {                                                                                         \
-    hipLaunchKernelGGL((k_combine_bf16<BM, BN, true, false>), dim3(n), dim3(256), 0, s, a, tiles, n, src_x,  \
+    hipLaunchKernelGGL((k_combine_bf16<BM, BN, true, false>), dim3(n), dim3(GemmT<BM, BN>::NT), 0, s, a, tiles, n, src_x,  \
                        dst_x, f, cf);                                                                        \
   } else {                                                                                                   \
-    hipLaunchKernelGGL((k_combine_bf16<BM, BN, false, false>), dim3(n), dim3(256), 0, s, a, tiles, n, src_x, \
+    hipLaunchKernelGGL((k_combine_bf16<BM, BN, false, false>), dim3(n), dim3(GemmT<BM, BN>::NT), 0, s, a, tiles, n, src_x, \
                        dst_x, f, cf);                                                                        \
   }
   if (bm == 256 && bn == 256) {
