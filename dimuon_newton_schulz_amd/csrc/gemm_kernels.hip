@@ -208,12 +208,26 @@ __device__ __forceinline__ void mma_bf16(const uint16_t* Pg, int64_t ldp, const 
       for (int t = 0; t < NS; ++t) rb[t] = *reinterpret_cast<const bf16x8_t*>(buf + b_off + t * 32 * LBK + ch);
     }
   };
+  // The combine (k-major Q, twice the LDS read instructions per B fragment)
+  // raises a wave's priority while it issues MFMAs, so that of the two waves
+  // on a SIMD the one with MFMAs ready issues first (6% faster combines; the
+  // symmetric products measured 1% slower with it).
   auto mfma_step = [&](const bf16x8_t (&ra)[MS], const bf16x8_t (&rb)[NS]) {
+    if constexpr (QT) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int s = 0; s < MS; ++s)
 #pragma unroll
       for (int t = 0; t < NS; ++t)
         acc[s][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[s], rb[t], acc[s][t], 0, 0, 0);
+    if constexpr (QT) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   // The point after which stage kt's buffer may be reloaded: this wave's
   // reads of it are complete and stage kt+1 has landed; no load is in flight.
