@@ -298,6 +298,8 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
     } else {
       d.KP = static_cast<int32_t>(round_up(d.k, kPad));
       d.NP = static_cast<int32_t>(round_up(d.N, kPad));
+      d.mpad = d.tall ? d.NP : d.KP;
+      d.npad = d.tall ? d.KP : d.NP;
       d.ncb = static_cast<int32_t>(ceil_div(d.n, 512));
       d.nrb = static_cast<int32_t>(ceil_div(d.m, 32));
       d.n_pn = (d.KP / 64) * (d.NP / 64);
@@ -308,7 +310,7 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
         for (int tj = 0; tj < d.NP / 64; ++tj) p.k3.push_back({static_cast<uint16_t>(i), (uint16_t)ti, (uint16_t)tj, 0});
       for (int ti = 0; ti < ceil_div(d.m, 64); ++ti)
         for (int tj = 0; tj < ceil_div(d.n, 64); ++tj) p.k5.push_back({static_cast<uint16_t>(i), (uint16_t)ti, (uint16_t)tj, 0});
-      d.ncond = static_cast<int32_t>(ceil_div(round_up(d.m, kPad) + round_up(d.n, kPad), 256));
+      d.ncond = static_cast<int32_t>(ceil_div(d.mpad + d.npad, 256));
       for (int c = 0; c < d.ncond; ++c) p.cond.push_back({static_cast<uint16_t>(i), static_cast<uint16_t>(c), 0, 0});
     }
   }
@@ -358,8 +360,8 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
     d.b_off = take(static_cast<size_t>(d.KP) * d.KP * es);
     d.z_off = take(kn * es);
     if (cfg->nesterov) d.v_off = take(static_cast<size_t>(d.m) * d.n * 4);
-    d.dr_off = take(static_cast<size_t>(round_up(d.m, kPad)) * 4);
-    d.dc_off = take(static_cast<size_t>(round_up(d.n, kPad)) * 4);
+    d.dr_off = take(static_cast<size_t>(d.mpad) * 4);
+    d.dc_off = take(static_cast<size_t>(d.npad) * 4);
     d.cm_off = take(static_cast<size_t>(d.ncond) * 8);
     d.pr_off = take(static_cast<size_t>(d.ncb) * d.m * 4);
     d.pc_off = take(static_cast<size_t>(d.nrb) * d.n * 4);

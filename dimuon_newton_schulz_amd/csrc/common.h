@@ -43,10 +43,11 @@ struct alignas(16) MatDesc {
   int64_t b_off;          // B = bA + c A A, KP x KP, ns dtype
   int64_t z_off;          // Z (last iterate), KP x NP (transposed for tall), ns dtype
   int64_t v_off;          // Nesterov input, m x n f32 (or -1)
-  int64_t dr_off;         // row factors, round_up(m, kPad) f32 (zero beyond m)
-  int64_t dc_off;         // column factors, round_up(n, kPad) f32 (zero beyond n)
+  int64_t dr_off;         // row factors, mpad f32 (zero beyond m)
+  int64_t dc_off;         // column factors, npad f32 (zero beyond n)
   int64_t cm_off;         // conditioning chunk maxima [ncond][2] f32 (rows, columns)
   int32_t ncond;          // conditioning chunks of 256 over the padded rows, then columns
+  int32_t mpad, npad;     // padded m and n: KP and NP in the caller's orientation
   int64_t pr_off;         // row-energy partials [ncb][m] f32
   int64_t pc_off;         // column-energy partials [nrb][n] f32
   int64_t pn_off;         // ||Y||^2 partials, one per prescale tile, f32

@@ -169,14 +169,13 @@ __device__ float block_max(float v, float* sh) {
   return r;
 }
 
-__device__ __forceinline__ int64_t pad_up(int64_t x) { return (x + kPad - 1) / kPad * kPad; }
 
 __global__ __launch_bounds__(256) void k_cond_energy(StepArgs a, const Tile* __restrict__ tiles) {
   __shared__ float sh[8];
   const Tile t = tiles[blockIdx.x];
   const MatDesc& d = a.desc[t.mat];
   const int m = d.m, n = d.n;
-  const int mp = static_cast<int>(pad_up(m));
+  const int mp = d.mpad;
   const int idx = t.ti * 256 + threadIdx.x;
   MUON_GLOBAL float* dr = gmem(reinterpret_cast<float*>(a.ws + d.dr_off));
   MUON_GLOBAL float* dc = gmem(reinterpret_cast<float*>(a.ws + d.dc_off));
@@ -195,7 +194,7 @@ __global__ __launch_bounds__(256) void k_cond_energy(StepArgs a, const Tile* __r
     }
     dr[i] = e;
     rmax = e;
-  } else if (idx < mp + pad_up(n)) {
+  } else if (idx < mp + d.npad) {
     const int j = idx - mp;
     float e = 0.0f;
     if (j < n) {
@@ -222,7 +221,7 @@ __global__ __launch_bounds__(256) void k_cond_factor(StepArgs a, const Tile* __r
   const Tile t = tiles[blockIdx.x];
   const MatDesc& d = a.desc[t.mat];
   const int m = d.m, n = d.n;
-  const int mp = static_cast<int>(pad_up(m));
+  const int mp = d.mpad;
   const MUON_GLOBAL float* cm = gmem(reinterpret_cast<const float*>(a.ws + d.cm_off));
   float rmax = 0.0f, cmax = 0.0f;
   for (int c = threadIdx.x; c < d.ncond; c += blockDim.x) {
@@ -237,7 +236,7 @@ __global__ __launch_bounds__(256) void k_cond_factor(StepArgs a, const Tile* __r
   if (idx < mp) {
     MUON_GLOBAL float* dr = gmem(reinterpret_cast<float*>(a.ws + d.dr_off));
     if (idx < m) dr[idx] = on ? cond_factor(dr[idx], rmax, a.eps) : 1.0f;
-  } else if (idx < mp + pad_up(n)) {
+  } else if (idx < mp + d.npad) {
     MUON_GLOBAL float* dc = gmem(reinterpret_cast<float*>(a.ws + d.dc_off));
     const int j = idx - mp;
     if (j < n) dc[j] = on ? cond_factor(dc[j], cmax, a.eps) : 1.0f;

@@ -82,6 +82,11 @@ def test_workspace_sizes():
     assert st == 0 and big32 >= 4096 * 4096 * 4 * (4 + 2 + 1)
     st, ragged = _ws_bytes(_mats([(300, 700)]), 1, c)
     assert st == 0 and ragged >= 384 * 768 * 2 * 4
+    # A Gram side of 1408 (an odd multiple of 128) stays 1408: X twice, A,
+    # B and Z, and nothing padded to 1536.
+    st, moe = _ws_bytes(_mats([(1408, 2048)]), 1, c)
+    assert st == 0 and 2 * (2 * 1408 * 2048 + 2 * 1408 * 1408 + 1408 * 2048) <= moe < \
+        2 * (2 * 1536 * 2048 + 2 * 1536 * 1536 + 1536 * 2048)
 
 
 @pytest.mark.parametrize("kind", ["null_mats", "count0", "zero_dim", "too_big", "steps", "dtype", "eps",

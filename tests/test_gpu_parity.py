@@ -167,6 +167,15 @@ def test_combine_tail_tiles(variant):
     run_case(wl, variant, cfg, indices=[0, wl.count - 1])
 
 
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
+def test_moe_expert_full_size(variant):
+    # One MoE expert at full size: 2048 x 1408 and 1408 x 2048.  The Gram
+    # side 1408 is an odd multiple of 128, so the combine runs 128 x 256
+    # tiles (eight waves) and the symmetric products 128 x 128 ones.
+    wl = W.moe_experts(experts=1, d_model=2048, d_ff=1408, seed=11)
+    run_case(wl, variant, cfg_of(wl))
+
+
 def test_moe_scaled_zero_rows():
     wl = W.moe_experts(experts=2, d_model=384, d_ff=264, seed=7)
     gpu, _ = run_case(wl, "dimuon", cfg_of(wl))
