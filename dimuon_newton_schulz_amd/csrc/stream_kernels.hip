@@ -428,41 +428,45 @@ __global__ __launch_bounds__(256) void k_update(StepArgs a, const Tile* __restri
   const float* dc = reinterpret_cast<const float*>(a.ws + d.dc_off);
   const float rf = a.dimuon ? dr[row] : 1.0f;
   const int64_t off = static_cast<int64_t>(row) * n;
+  // Both halves are loaded (W, Z and the column factors) before the first
+  // store, which the compiler would otherwise have to order them after.
+  float w[2][8], zv[2][8], cf[2][8];
+#pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int col0 = t.tj * 64 + c0 + 8 * h;
-    if (col0 >= n) break;
-    float w[8], o[8];
-    load8(d.w, a.w_dt, off, col0, n, w);
-    float zv[8];
+    if (col0 >= n) continue;
+    load8(d.w, a.w_dt, off, col0, n, w[h]);
     const int64_t zi = static_cast<int64_t>(row) * zld + col0;
     if (a.ns_dt == DT_F32) {
       const float4* zq = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.ws + d.z_off) + zi);
       const float4 z0 = zq[0], z1 = zq[1];
-      zv[0] = z0.x; zv[1] = z0.y; zv[2] = z0.z; zv[3] = z0.w;
-      zv[4] = z1.x; zv[5] = z1.y; zv[6] = z1.z; zv[7] = z1.w;
+      zv[h][0] = z0.x; zv[h][1] = z0.y; zv[h][2] = z0.z; zv[h][3] = z0.w;
+      zv[h][4] = z1.x; zv[h][5] = z1.y; zv[h][6] = z1.z; zv[h][7] = z1.w;
     } else {
       const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.ws + d.z_off) + zi);
       const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        zv[2 * e] = __uint_as_float(w4[e] << 16);
-        zv[2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
+        zv[h][2 * e] = __uint_as_float(w4[e] << 16);
+        zv[h][2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
       }
     }
 #pragma unroll
+    for (int e = 0; e < 8; ++e) cf[h][e] = (a.dimuon && col0 + e < n) ? dc[col0 + e] : 1.0f;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int col0 = t.tj * 64 + c0 + 8 * h;
+    if (col0 >= n) continue;
+    float o[8];
+#pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int col = col0 + e;
-      if (a.dimuon) {
-        const float cf = (col < n) ? dc[col] : 1.0f;
-        o[e] = sc.post * ((rf * zv[e]) * cf);
-      } else {
-        o[e] = zv[e];
-      }
+      o[e] = a.dimuon ? sc.post * ((rf * zv[h][e]) * cf[h][e]) : zv[h][e];
       // W - lr * (scale * O + wd * W), with the outer product-subtract fused.
-      const float upd = __builtin_fmaf(d.update_scale, o[e], a.weight_decay * w[e]);
-      w[e] = __builtin_fmaf(-a.lr, upd, w[e]);
+      const float upd = __builtin_fmaf(d.update_scale, o[e], a.weight_decay * w[h][e]);
+      w[h][e] = __builtin_fmaf(-a.lr, upd, w[h][e]);
     }
-    store8(d.w, a.w_dt, off, col0, n, w);
+    store8(d.w, a.w_dt, off, col0, n, w[h]);
     if (d.o_out) store8(d.o_out, DT_F32, off, col0, n, o);
   }
 }
