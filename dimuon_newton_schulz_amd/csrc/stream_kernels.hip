@@ -73,7 +73,10 @@ __device__ __forceinline__ void store8(void* p, int32_t dt, int64_t rowoff, int 
 // four waves pairwise -> pc[rb][col].  Both are aligned power-of-two blocks
 // of the stated tree.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_momentum(StepArgs a, const Tile* __restrict__ tiles,
+// Eight waves per SIMD (64 VGPRs; the default allocation took 66 and seven
+// waves): the row-at-a-time loop keeps one row of M and G in flight per
+// wave, so waves are what keep the memory system busy.
+__global__ __launch_bounds__(256, 8) void k_momentum(StepArgs a, const Tile* __restrict__ tiles,
                                                   int energies) {
   __shared__ float red[4][512];
   const Tile t = tiles[blockIdx.x];
