@@ -168,6 +168,16 @@ def test_combine_tail_tiles(variant):
 
 
 @pytest.mark.parametrize("variant", ["muon", "dimuon"])
+def test_combine_256x128_tiles(variant):
+    # Gram side 512 (a multiple of 256), long side 1408 (an odd multiple of
+    # 128): the combine runs 256 x 128 tiles (eight waves, one 32-column
+    # block per wave), wide and tall matrices alike.
+    shapes = [(512, 1408)] * 4 + [(1408, 512)] * 2
+    wl = W.random_batch(shapes, dtype="bf16", ns_dtype="bf16", seed=12, variant=variant)
+    run_case(wl, variant, cfg_of(wl), indices=[0, 3, 4, 5])
+
+
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
 def test_moe_expert_full_size(variant):
     # One MoE expert at full size: 2048 x 1408 and 1408 x 2048.  The Gram
     # side 1408 is an odd multiple of 128, so the combine runs 128 x 256
