@@ -140,8 +140,8 @@ __device__ __forceinline__ void issue_stage(const MUON_GLOBAL uint16_t* P, int64
   }
 }
 
-// acc[s][t] += sum over k < K of P[row wr*BM/2 + s*32 + i][k] * Q(k, col wc*BN/2 + t*32 + j),
-// with Q(k, n) = Q[n][k] (n-major, QT false) or Q[k][n] (k-major, QT true);
+// acc[s][t] += sum over k < K of P[row wr*BM/2 + s*32 + i][k] * Q(k, col wc*BN/WC + t*32 + j),
+// (wave = wr * WC + wc) with Q(k, n) = Q[n][k] (n-major, QT false) or Q[k][n] (k-major, QT true);
 // K is a multiple of 2 * LBK.  A stage holds NQ k-steps of 16; the two
 // stages alternate between buffers b0 and b1 (the loop is unrolled by two,
 // so every access names its buffer).  Per stage kt, with fragments read one
