@@ -42,21 +42,52 @@ MEASURED_TRAFFIC = {
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
+# The same counters for the combine kernel of the GEMM workloads (one
+# iteration before the last; a product with a tail launch lists both
+# launches), plus the matrix-core counters of that kernel: bf16 MFMA busy
+# cycles over the active cycles of the 1024 SIMDs (GRBM_GUI_ACTIVE summed
+# over the 8 XCDs, divided by 8), and the clock those active cycles imply.
+# Valid only for the GEMM and planner sources they were taken on; figures
+# and commands in profiles/gemm_counters_gpt2_square_moe.md (the square set
+# was counted on N(0,1) inputs of the same shapes: the readings do not
+# depend on the values).
+GEMM_SOURCES = ("dimuon_newton_schulz_amd/csrc/gemm_kernels.hip", "dimuon_newton_schulz_amd/csrc/api.hip",
+                "dimuon_newton_schulz_amd/csrc/common.h")
+MEASURED_GEMM = {
+    "sources_sha256": "893dfcc0c8f5dde2fdf2842003b0b36f0f82cbb5a0684a5fc347a12a680f5384",
+    "gpt2_small_12x4_bf16": {"fetch_kib": [134134.6, 5246.8], "write_kib": [163840.0, 2048.0],
+                             "mfma_busy_frac": 0.358, "clock_ghz": 2.19},
+    "square_8x4096x4096_bf16": {"fetch_kib": [786716.5], "write_kib": [262144.3],
+                                "mfma_busy_frac": 0.531, "clock_ghz": 1.96},
+    "moe_64x(2048x1408+1408x2048)_bf16": {"fetch_kib": [1470754.6], "write_kib": [720896.0],
+                                          "mfma_busy_frac": 0.370, "clock_ghz": 1.99},
+}
 
-def thin_sources_sha():
+
+def sources_sha(rels):
     import hashlib
     h = hashlib.sha256()
-    for rel in THIN_SOURCES:
+    for rel in rels:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def measured_gemm(workload):
+    """Counter figures of a GEMM workload's combine (HBM bytes per iteration,
+    matrix-core busy fraction), or None if the sources changed since."""
+    rec = MEASURED_GEMM.get(workload)
+    if rec is None or sources_sha(GEMM_SOURCES) != MEASURED_GEMM["sources_sha256"]:
+        return None
+    nbytes = sum(f * FETCH_SCALE + w * WRITE_SCALE for f, w in zip(rec["fetch_kib"], rec["write_kib"])) * 1024
+    return {"traffic": int(round(nbytes)), "mfma_busy_frac": rec["mfma_busy_frac"], "clock_ghz": rec["clock_ghz"]}
 
 
 def measured_traffic(kernel):
     """HBM bytes per launch from the committed counter runs, or None if the
     kernel sources changed since they were taken."""
     rec = MEASURED_TRAFFIC.get(kernel)
-    if rec is None or thin_sources_sha() != MEASURED_TRAFFIC["sources_sha256"]:
+    if rec is None or sources_sha(THIN_SOURCES) != MEASURED_TRAFFIC["sources_sha256"]:
         return None
     return int(round((rec["fetch_kib"] * FETCH_SCALE + rec["write_kib"] * WRITE_SCALE) * 1024))
 
@@ -74,15 +105,22 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="buffer sets rotated (0: automatic)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gaussian-inputs", action="store_true",
+                    help="c4 only: N(0,1) gradients and momenta of the same shapes instead of the "
+                         "prescribed-spectrum ones (no QR in the input set-up; for counter runs, whose "
+                         "kernel readings do not depend on the values)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="bytes of a plain device-to-device copy run once before the workload "
                          "(calibrates HBM byte counters against a known size)")
     return ap.parse_args()
 
 
-def make_workload(name, device, variant=None):
+def make_workload(name, device, variant=None, gaussian=False):
     import workloads as W
-    if name == "c1":
+    if name == "c4" and gaussian:
+        wl = W.random_batch([(4096, 4096)] * 8, device=device, variant=variant or "dimuon")
+        wl.name = "square_8x4096x4096_bf16_gaussian"
+    elif name == "c1":
         wl = W.lora_toy(seed=0, device=device)
     elif name == "c2":
         wl = W.lora_batch(device=device)
@@ -230,6 +268,13 @@ def roofline_for(wl, cfg, per_kind, work, steps):
         out["flops_per_launch"] = flops
     else:
         out["flops_per_iteration"] = flops
+    counted = measured_gemm(wl.name.replace("_gaussian", "")) if kind == "combine" else None
+    if counted is not None:
+        out["traffic"] = counted["traffic"]
+        if per_iter != 1:
+            out["traffic_basis"] = "per iteration (all launches of the product)"
+        out["counters"] = {"mfma_busy_frac": counted["mfma_busy_frac"], "clock_ghz": counted["clock_ghz"],
+                           "source": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE"}
     return kind, out
 
 
@@ -297,7 +342,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     variant = args.variant or ("muon" if args.config == "c3" else "dimuon")
-    wl = make_workload(args.config, dev, variant)
+    wl = make_workload(args.config, dev, variant, gaussian=args.gaussian_inputs)
     work = algorithmic(wl, is_thin)
     full_count = wl.count
     sets = args.sets or (4 if work["hbm_bytes_min"] < 300e6 else 1)
