@@ -123,6 +123,17 @@ def test_general_f32_storage(variant):
     run_case(wl, variant, cfg_of(wl))
 
 
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
+def test_maximum_extent(variant):
+    # Long sides at the supported maximum of 65536, wide and tall: thin Gram
+    # sides 8 and 32 (128 and 256 slices, the most a matrix may have) and a
+    # general Gram side of 33 (padded to 128; its Gram is a product over
+    # K = 65536), next to the thin path's largest Gram side.
+    shapes = [(8, 65536), (65536, 32), (33, 65536), (65536, 40)]
+    wl = W.random_batch(shapes, dtype="bf16", ns_dtype="bf16", seed=11, variant=variant)
+    run_case(wl, variant, cfg_of(wl))
+
+
 def test_gpt2_shapes_scaled():
     wl = W.gpt2_hidden(layers=1, d_model=256, seed=5)
     run_case(wl, "muon", cfg_of(wl))
