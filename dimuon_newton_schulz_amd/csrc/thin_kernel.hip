@@ -914,8 +914,12 @@ __device__ __forceinline__ void pass_b_body(const StepArgs& args, const MatDesc&
   };
 
   if constexpr (KP <= 8) {
+    // Wave 0's partial loads are issued before any slice load of the
+    // workgroup (the barrier waits for issue, not for data), so that they
+    // travel ahead of the slice traffic.
+    if (wave == 0) load_partials(tid, 0);
+    __builtin_amdgcn_s_barrier();
     if (wave == 0) {
-      load_partials(tid, 0);
       sum_partials();
       wave_lds_sync();
       const double in0 = inv_norm();
