@@ -554,6 +554,9 @@ __device__ __forceinline__ void pass_a_core(const StepArgs& args, const MatDesc&
     if (tid < d.S) smax = gmem(cin.smax)[tid];   // S <= TT
 #pragma unroll
     for (int e = 0; e < VEC; ++e) pe[e] = (l0 + e < N) ? gmem(cin.pos)[l0 + e] : 0.0f;
+    // Every wave's cache loads are issued before any slice load of the
+    // workgroup (the barrier waits for issue, not for data).
+    __builtin_amdgcn_s_barrier();
   }
 
   slice_load<KP, TALL>(d.mom, args.mom_dt, k, N, n, l0, full, y);   // M_{t-1}, then M_t
