@@ -54,13 +54,13 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 GEMM_SOURCES = ("dimuon_newton_schulz_amd/csrc/gemm_kernels.hip", "dimuon_newton_schulz_amd/csrc/api.hip",
                 "dimuon_newton_schulz_amd/csrc/common.h")
 MEASURED_GEMM = {
-    "sources_sha256": "893dfcc0c8f5dde2fdf2842003b0b36f0f82cbb5a0684a5fc347a12a680f5384",
-    "gpt2_small_12x4_bf16": {"fetch_kib": [134134.6, 5246.8], "write_kib": [163840.0, 2048.0],
-                             "mfma_busy_frac": 0.358, "clock_ghz": 2.19},
-    "square_8x4096x4096_bf16": {"fetch_kib": [786716.5], "write_kib": [262144.3],
-                                "mfma_busy_frac": 0.531, "clock_ghz": 1.96},
-    "moe_64x(2048x1408+1408x2048)_bf16": {"fetch_kib": [1470754.6], "write_kib": [720896.0],
-                                          "mfma_busy_frac": 0.370, "clock_ghz": 1.99},
+    "sources_sha256": "624029b651cc1598d5288b69a86c60ef7186e77af00bb51b3bc89310be51b1cc",
+    "gpt2_small_12x4_bf16": {"fetch_kib": [134150.1, 5246.8], "write_kib": [163840.0, 2048.0],
+                             "mfma_busy_frac": 0.359, "clock_ghz": 2.19},
+    "square_8x4096x4096_bf16": {"fetch_kib": [786674.3], "write_kib": [262144.0],
+                                "mfma_busy_frac": 0.542, "clock_ghz": 1.89},
+    "moe_64x(2048x1408+1408x2048)_bf16": {"fetch_kib": [1470199.3], "write_kib": [720896.0],
+                                          "mfma_busy_frac": 0.376, "clock_ghz": 1.97},
 }
 
 

@@ -172,7 +172,10 @@ __device__ __forceinline__ void mma_bf16(const uint16_t* Pg, int64_t ldp, const 
   const MUON_GLOBAL uint16_t* P = gmem(Pg);
   const MUON_GLOBAL uint16_t* Q = gmem(Qg);
   const int nk = K / LBK;
+  // Every wave's stage-0 loads are issued before any stage-1 load (the
+  // barrier waits for issue, not for data): the first stage arrives first.
   issue_stage<BM, BN, QT>(P, ldp, Q, ldq, 0, b0);
+  __builtin_amdgcn_s_barrier();
   issue_stage<BM, BN, QT>(P, ldp, Q, ldq, 1, b1);
   // Fragment addresses (elements within a stage): row (lane & 31) of each
   // 32-row block, logical chunk 2 q + (lane >> 5) for k-step q.  The swizzle
