@@ -113,9 +113,11 @@ __device__ __forceinline__ int qswz(int row) { return 4 * (row & 3); }
 // wave's load writes 64 consecutive 16-byte LDS chunks (8 rows of P, or of Q
 // when n-major; 512 / BN k-rows of Q when k-major); each lane fetches the
 // global chunk that belongs in its slot.
+// same: Q is P (a diagonal tile of a symmetric product); only P's rows are
+// loaded, and the fragments of both operands come from them.
 template <int BM, int BN, bool QT>
 __device__ __forceinline__ void issue_stage(const MUON_GLOBAL uint16_t* P, int64_t ldp, const MUON_GLOBAL uint16_t* Q,
-                                            int64_t ldq, int st, uint16_t* buf) {
+                                            int64_t ldq, int st, uint16_t* buf, bool same = false) {
   using G = GemmT<BM, BN>;
   constexpr int LPR = BN / 8, RPI = 64 / LPR;   // k-major Q: lanes per k-row, k-rows per load
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -123,6 +125,7 @@ __device__ __forceinline__ void issue_stage(const MUON_GLOBAL uint16_t* P, int64
 #pragma unroll
   for (int q = 0; q < G::LA + G::LB; ++q) {
     const bool is_a = q < G::LA;
+    if (!is_a && same) break;
     const int blk = (is_a ? q : q - G::LA) * G::NW + wave;
     const MUON_GLOBAL uint16_t* src;
     if (QT && !is_a) {
@@ -163,7 +166,8 @@ __device__ __forceinline__ void issue_stage(const MUON_GLOBAL uint16_t* P, int64
 template <int BM, int BN, bool QT>
 __device__ __forceinline__ void mma_bf16(const uint16_t* Pg, int64_t ldp, const uint16_t* Qg, int64_t ldq, int K,
                                          uint16_t* b0, uint16_t* b1,
-                                         f32x16_t (&acc)[GemmT<BM, BN>::MS][GemmT<BM, BN>::NS]) {
+                                         f32x16_t (&acc)[GemmT<BM, BN>::MS][GemmT<BM, BN>::NS],
+                                         bool same = false) {
   using G = GemmT<BM, BN>;
   constexpr int MS = G::MS, NS = G::NS, LPS = G::LPS, WN = BN / G::WC;
   static_assert(NQ % 2 == 0, "fragment sets alternate");
@@ -174,14 +178,14 @@ __device__ __forceinline__ void mma_bf16(const uint16_t* Pg, int64_t ldp, const 
   const int nk = K / LBK;
   // Every wave's stage-0 loads are issued before any stage-1 load (the
   // barrier waits for issue, not for data): the first stage arrives first.
-  issue_stage<BM, BN, QT>(P, ldp, Q, ldq, 0, b0);
+  issue_stage<BM, BN, QT>(P, ldp, Q, ldq, 0, b0, same);
   __builtin_amdgcn_s_barrier();
-  issue_stage<BM, BN, QT>(P, ldp, Q, ldq, 1, b1);
+  issue_stage<BM, BN, QT>(P, ldp, Q, ldq, 1, b1, same);
   // Fragment addresses (elements within a stage): row (lane & 31) of each
   // 32-row block, logical chunk 2 q + (lane >> 5) for k-step q.  The swizzle
   // of a row depends on its index mod 16 only, i.e. on lane & 31.
   const int fr = lane & 31, sw = swz(fr), half = lane >> 5;
-  const int a_off = (wr * (BM / 2) + fr) * LBK, b_off = BM * LBK + (wc * WN + fr) * LBK;
+  const int a_off = (wr * (BM / 2) + fr) * LBK, b_off = (same ? 0 : BM * LBK) + (wc * WN + fr) * LBK;
   // k-major Q: the reading lane's k-row and n-column in the stage (block t
   // adds 32 columns, k-step q 16 rows, the second read 4 rows); the swizzle
   // of those rows is 4 (m / 4) throughout.
@@ -249,7 +253,7 @@ __device__ __forceinline__ void mma_bf16(const uint16_t* Pg, int64_t ldp, const 
   // is entered and closed at a sync, with no load in flight, so the compiler
   // keeps track of which buffer the loads in flight write.
   auto half_step = [&](uint16_t* cur, uint16_t* nxt, int kt) {
-    if (kt + 2 < nk) issue_stage<BM, BN, QT>(P, ldp, Q, ldq, kt + 2, cur);
+    if (kt + 2 < nk) issue_stage<BM, BN, QT>(P, ldp, Q, ldq, kt + 2, cur, same);
     read_step(nxt, 0, fa[0], fb[0]);
     mfma_step(fa[(NQ - 1) & 1], fb[(NQ - 1) & 1]);
 #pragma unroll
@@ -260,7 +264,8 @@ __device__ __forceinline__ void mma_bf16(const uint16_t* Pg, int64_t ldp, const 
     sync();
   };
   // Stage 0 landed (stage 1's loads were issued after it).
-  wait_vm<LPS>();
+  if (same) wait_vm<G::LA>();
+  else wait_vm<LPS>();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   read_step(b0, 0, fa[0], fb[0]);
@@ -464,8 +469,9 @@ __global__ __launch_bounds__((GemmT<BT, BT>::NT), 1) void k_syrk_bf16(StepArgs a
     for (int u = 0; u < G::NS; ++u)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[s][u][r] = 0.0f;
+  // A diagonal tile multiplies a panel by itself: it is loaded once.
   mma_bf16<BT, BT, false>(P + static_cast<int64_t>(t.ti) * BT * ld, ld, P + static_cast<int64_t>(t.tj) * BT * ld, ld,
-                          static_cast<int>(ld), sm.buf[0], sm.buf[1], acc);
+                          static_cast<int>(ld), sm.buf[0], sm.buf[1], acc, t.ti == t.tj);
 
   const float alpha = (kind == 0) ? (first ? a.scal[d.scal_idx].inv_nu2 : 1.0f) : cf.c;
   const uint16_t* E = reinterpret_cast<const uint16_t*>(a.ws + d.a_off);
