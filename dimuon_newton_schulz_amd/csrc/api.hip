@@ -191,6 +191,41 @@ void add_tiles(std::vector<Tile>& out, uint16_t mat, int rows, int cols, bool up
         if (!upper || ti <= tj) out.push_back({mat, static_cast<uint16_t>(ti), static_cast<uint16_t>(tj), 0});
 }
 
+// Matrix order for a symmetric product's tile list of bt x bt tiles.  Each
+// XCD walks a contiguous run of the list (equal tile counts per run), and a
+// tile's work is its K (the padded long side for the Gram), which differs
+// between matrices of one batch: matrices are placed largest K first, each
+// into the run with the least work that still has room for all its tiles.
+// Returns the given order when the matrices do not pack into the runs.
+std::vector<uint16_t> xcd_balanced_order(const Plan& p, int bt) {
+  constexpr int kXcds = 8;
+  std::vector<uint16_t> order = p.gen;
+  auto tiles_of = [&](uint16_t i) {
+    const int64_t rb = p.desc[i].KP / bt;
+    return rb * (rb + 1) / 2;
+  };
+  int64_t n = 0;
+  for (uint16_t i : order) n += tiles_of(i);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](uint16_t x, uint16_t y) { return p.desc[x].NP > p.desc[y].NP; });
+  std::vector<int64_t> room(kXcds), work(kXcds, 0);
+  for (int x = 0; x < kXcds; ++x) room[x] = n / kXcds + (x < n % kXcds ? 1 : 0);
+  std::vector<std::vector<uint16_t>> runs(kXcds);
+  for (uint16_t i : order) {
+    const int64_t t = tiles_of(i);
+    int best = -1;
+    for (int x = 0; x < kXcds; ++x)
+      if (room[x] >= t && (best < 0 || work[x] < work[best])) best = x;
+    if (best < 0) return p.gen;
+    runs[best].push_back(i);
+    room[best] -= t;
+    work[best] += t * p.desc[i].NP;
+  }
+  order.clear();
+  for (const auto& r : runs) order.insert(order.end(), r.begin(), r.end());
+  return order;
+}
+
 void plan_gemm_tiles(Plan& p, bool bf16) {
   auto side = [&](int32_t x, bool big) { return (big && x % 256 == 0) ? 256 : 128; };
   auto rounds_time = [&](const std::map<std::pair<int, int>, int64_t>& n) {
@@ -218,7 +253,9 @@ void plan_gemm_tiles(Plan& p, bool bf16) {
     }
     auto& lists = kind == 0 ? p.syrk : p.comb;
     std::map<std::pair<int, int>, size_t> at;
-    for (uint16_t i : p.gen) {
+    // 128 x 128 symmetric tiles (no tail split follows): runs balanced by K.
+    const std::vector<uint16_t> order = (kind == 0 && !big) ? xcd_balanced_order(p, 128) : p.gen;
+    for (uint16_t i : order) {
       MatDesc& d = p.desc[i];
       const int bm = side(d.KP, big), bn = kind == 0 ? bm : side(d.NP, big);
       auto it = at.find({bm, bn});
