@@ -205,7 +205,12 @@ std::vector<uint16_t> xcd_balanced_order(const Plan& p, int bt) {
     return rb * (rb + 1) / 2;
   };
   int64_t n = 0;
-  for (uint16_t i : order) n += tiles_of(i);
+  bool uniform = true;
+  for (uint16_t i : order) {
+    n += tiles_of(i);
+    uniform = uniform && p.desc[i].NP == p.desc[order[0]].NP && p.desc[i].KP == p.desc[order[0]].KP;
+  }
+  if (uniform) return order;   // equal runs already carry equal work
   std::stable_sort(order.begin(), order.end(),
                    [&](uint16_t x, uint16_t y) { return p.desc[x].NP > p.desc[y].NP; });
   std::vector<int64_t> room(kXcds), work(kXcds, 0);
