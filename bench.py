@@ -105,6 +105,7 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="buffer sets rotated (0: automatic)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-toy", action="store_true", help="skip the 4 x 16 toy's column-share report")
     ap.add_argument("--gaussian-inputs", action="store_true",
                     help="c4 only: N(0,1) gradients and momenta of the same shapes instead of the "
                          "prescribed-spectrum ones (no QR in the input set-up; for counter runs, whose "
@@ -296,6 +297,54 @@ def host_sample(name, variant):
     return wl
 
 
+TOY_SEEDS = 32
+
+
+def top4_share(o):
+    """Share of the squared step in the four largest-scale columns (the last
+    four of the toy's geometric column grid)."""
+    col = (o ** 2).sum(0)
+    return float(col[-4:].sum() / col.sum())
+
+
+def toy_report(dev):
+    """The 4 x 16 LoRA toy's report ("Dimuon: LoRA 에 맞춰 다시 짠 Muon",
+    the toy with sixteen input columns of scale 0.1 .. 10): the share of the
+    squared step in the four largest-scale columns and sigma_max / sigma_min
+    of the step, for Muon and Dimuon, from the GPU path over seeded draws.
+    The pages' figures (one unknown seed, a different orthogonaliser) are
+    carried beside them as context."""
+    import numpy as np
+    import torch
+    import dimuon_newton_schulz_amd as D
+    import workloads as W
+
+    wls = [W.lora_toy(seed=s, device=dev) for s in range(TOY_SEEDS)]
+    wl0 = wls[0]
+    cfg = D.StepConfig(lr=wl0.lr, momentum=wl0.mu, w_dtype=wl0.w_dtype, g_dtype=wl0.g_dtype,
+                       mom_dtype=wl0.mom_dtype, ns_dtype=wl0.ns_dtype)
+    out = {"workload": wl0.name, "seeds": TOY_SEEDS, "ns_dtype": wl0.ns_dtype}
+    shares = {}
+    for variant in ("muon", "dimuon"):
+        params = [D.Param(w=wl.mats[0].w.clone(), g=wl.mats[0].g.clone(), mom=wl.mats[0].m_prev.clone(),
+                          o_out=torch.empty(wl.mats[0].w.shape, dtype=torch.float32, device=dev)) for wl in wls]
+        (D.dimuon_step if variant == "dimuon" else D.muon_step)(params, cfg)
+        torch.cuda.synchronize()
+        os_ = [p.o_out.double().cpu().numpy() for p in params]
+        sh = [top4_share(o) for o in os_]
+        sv = [np.linalg.svd(o, compute_uv=False) for o in os_]
+        ratio = [float(v[0] / v[-1]) for v in sv]
+        shares[variant] = sh
+        out[variant] = {"top4_share_seed0": round(sh[0], 4), "top4_share_median": round(float(np.median(sh)), 4),
+                        "sigma_ratio_seed0": round(ratio[0], 3), "sigma_ratio_median": round(float(np.median(ratio)), 3)}
+    out["dimuon_below_muon_fraction"] = sum(d < m for d, m in zip(shares["dimuon"], shares["muon"])) / TOY_SEEDS
+    g0 = wl0.mats[0].g.double().cpu().numpy()
+    out["adam_first_step_top4_share"] = round(top4_share(np.sign(g0)), 4)
+    out["pages_context"] = {"muon_polar_express_top4_share": 0.71, "dimuon_top4_share": 0.19,
+                            "dimuon_sigma_ratio": 5.41, "adam_first_step_top4_share": 0.25}
+    return out
+
+
 def cpu_baseline(wl_host, full_count, seconds):
     """The oracle as it stands, on host cores, over a bounded sample of the batch."""
     import oracle as O
@@ -397,6 +446,8 @@ def main():
             del wl2
             torch.cuda.empty_cache()
     out["workloads"] = extras
+    if not args.no_toy:
+        out["toy_report"] = toy_report(dev)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(host_sample(args.config, variant), full_count, args.cpu_seconds)

@@ -71,6 +71,26 @@ def test_lora_toy_4x16_f32(variant):
     run_case(wl, variant, cfg_of(wl))
 
 
+def test_lora_toy_column_share_report():
+    # The toy's report quantity (share of the squared step in the four
+    # largest-scale columns) from the GPU step equals the oracle's, and
+    # Dimuon lowers it below Muon's on every seed.
+    def share(o):
+        col = (o ** 2).sum(0)
+        return col[-4:].sum() / col.sum()
+    for seed in range(8):
+        wl = W.lora_toy(seed=seed)
+        cfg = cfg_of(wl)
+        got = {}
+        for variant in ("muon", "dimuon"):
+            announce(f"{wl.name} seed {seed} {variant}: column share")
+            gpu = run_gpu(wl, variant, cfg)
+            ref = run_oracle(wl, variant, cfg, 0)
+            got[variant] = share(gpu.o[0])
+            assert abs(got[variant] - share(ref.o)) < 1e-5, (seed, variant, got[variant], share(ref.o))
+        assert got["dimuon"] < got["muon"], (seed, got)
+
+
 @pytest.mark.parametrize("variant", ["muon", "dimuon"])
 @pytest.mark.parametrize("ns", ["bf16", "f32"])
 def test_lora_batch_small(variant, ns):
