@@ -71,6 +71,11 @@ struct Plan {
   // GEMM tile lists, one launch each; bm x bn tiles (symmetric products: square)
   struct GemmList { int bm, bn; std::vector<Tile> tiles; size_t off; };
   std::vector<GemmList> syrk, comb;
+  // Combine lists of the iterations before the last (empty: same as comb),
+  // and the rows each matrix's iterates and B carry (KP, or KP rounded up to
+  // 256 when comb_mid runs it on 256-row tiles).
+  std::vector<GemmList> comb_mid;
+  std::vector<int32_t> rows;
   std::vector<uint16_t> gen;
   // thin matrices grouped by padded Gram side KP; one tile (matrix, slice)
   // per workgroup, one launch per phase and KP
@@ -306,6 +311,37 @@ void plan_gemm_tiles(Plan& p, bool bf16) {
       }
     }
   }
+  // Iterations before the last: a matrix whose padded Gram side is an odd
+  // multiple of 128 (at least 1024) runs the combine on 256 x 256 tiles over
+  // its rows rounded up to 256.  B and the iterates then carry 128 rows more;
+  // those rows of X' are written but never read (the Gram reads rows below
+  // KP, and so does the combine as its k operand), so they need no clearing.
+  // The last iteration keeps the lists above: Z, the norm partials and the
+  // padding of the result are those of the exact Gram side.
+  p.comb_mid.clear();
+  p.rows.assign(p.desc.size(), 0);
+  for (uint16_t i : p.gen) p.rows[i] = p.desc[i].KP;
+  bool big_comb = false;
+  for (const auto& l : p.comb) big_comb = big_comb || l.bm == 256 || l.bn == 256;
+  if (bf16 && big_comb) {
+    Plan::GemmList pad{256, 256, {}, 0};
+    for (uint16_t i : p.gen) {
+      const MatDesc& d = p.desc[i];
+      if (d.KP % 256 == 128 && d.KP >= 1024 && d.NP % 256 == 0) {
+        add_tiles(pad.tiles, i, (d.KP + 128) / 256, d.NP / 256, false);
+        p.rows[i] = d.KP + 128;
+      }
+    }
+    if (!pad.tiles.empty()) {
+      for (const auto& l : p.comb) {
+        Plan::GemmList c{l.bm, l.bn, {}, 0};
+        for (const Tile& t : l.tiles)
+          if (p.rows[t.mat] == p.desc[t.mat].KP) c.tiles.push_back(t);
+        if (!c.tiles.empty()) p.comb_mid.push_back(std::move(c));
+      }
+      p.comb_mid.push_back(std::move(pad));
+    }
+  }
 }
 
 // Builds the plan.  `with_table` also serialises the uploaded prefix.
@@ -373,6 +409,7 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
   p.k3_off = take(sizeof(Tile) * p.k3.size());
   for (auto& l : p.syrk) l.off = take(sizeof(Tile) * l.tiles.size());
   for (auto& l : p.comb) l.off = take(sizeof(Tile) * l.tiles.size());
+  for (auto& l : p.comb_mid) l.off = take(sizeof(Tile) * l.tiles.size());
   p.k5_off = take(sizeof(Tile) * p.k5.size());
   p.cond_off = take(sizeof(Tile) * p.cond.size());
   p.gen_off = take(sizeof(uint16_t) * p.gen.size());
@@ -396,10 +433,11 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
   for (uint16_t i : p.gen) {
     MatDesc& d = p.desc[i];
     const size_t kn = static_cast<size_t>(d.KP) * d.NP;
+    const size_t xn = static_cast<size_t>(p.rows[i]) * d.NP;   // iterates: rows the combine writes
     // X^T copies only for the fp32 products; the bf16 combine reads X itself.
-    for (int b = 0; b < 4; ++b) d.x_off[b] = ((b & 1) && cfg->ns_dtype == MUON_BF16) ? -1 : take(kn * es);
+    for (int b = 0; b < 4; ++b) d.x_off[b] = ((b & 1) && cfg->ns_dtype == MUON_BF16) ? -1 : take(xn * es);
     d.a_off = take(static_cast<size_t>(d.KP) * d.KP * es);
-    d.b_off = take(static_cast<size_t>(d.KP) * d.KP * es);
+    d.b_off = take(static_cast<size_t>(p.rows[i]) * d.KP * es);
     d.z_off = take(kn * es);
     if (cfg->nesterov) d.v_off = take(static_cast<size_t>(d.m) * d.n * 4);
     d.dr_off = take(static_cast<size_t>(d.mpad) * 4);
@@ -419,6 +457,7 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
     put(p.table, p.k3_off, p.k3);
     for (auto& l : p.syrk) put(p.table, l.off, l.tiles);
     for (auto& l : p.comb) put(p.table, l.off, l.tiles);
+    for (auto& l : p.comb_mid) put(p.table, l.off, l.tiles);
     put(p.table, p.k5_off, p.k5);
     put(p.table, p.cond_off, p.cond);
     put(p.table, p.gen_off, p.gen);
@@ -602,7 +641,7 @@ muon_status_t launch_all(const Plan& p, const StepArgs& a, const Coeffs* cf, int
         MUON_LAUNCH(MUON_LAUNCH_GRAM, launch_syrk(a, tl(l.off), nt(l), l.bm, 0, src, first, cf[t], s));
       for (const auto& l : p.syrk)
         MUON_LAUNCH(MUON_LAUNCH_POLY, launch_syrk(a, tl(l.off), nt(l), l.bm, 1, src, first, cf[t], s));
-      for (const auto& l : p.comb)
+      for (const auto& l : (last || p.comb_mid.empty()) ? p.comb : p.comb_mid)
         MUON_LAUNCH(MUON_LAUNCH_COMBINE,
                     launch_combine(a, tl(l.off), nt(l), l.bm, l.bn, src, dst, first, last, true, cf[t], s));
     }

@@ -209,6 +209,17 @@ def test_combine_256x128_tiles(variant):
 
 
 @pytest.mark.parametrize("variant", ["muon", "dimuon"])
+def test_combine_padded_rows(variant):
+    # Gram sides 1152 and 1408 (odd multiples of 128): the iterations before
+    # the last run the combine on 256 x 256 tiles over rows rounded up to
+    # 256, the last on the exact rows; a matrix with a small Gram side shares
+    # the batch.  The launch kinds show both combine lists in use.
+    shapes = [(1152, 2048), (2048, 1152), (1408, 1536), (300, 700)]
+    wl = W.random_batch(shapes, dtype="bf16", ns_dtype="bf16", seed=21, variant=variant)
+    run_case(wl, variant, cfg_of(wl))
+
+
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
 def test_moe_expert_full_size(variant):
     # One MoE expert at full size: 2048 x 1408 and 1408 x 2048.  The Gram
     # side 1408 is an odd multiple of 128, so the combine runs 128 x 256
