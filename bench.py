@@ -43,8 +43,8 @@ MEASURED_TRAFFIC = {
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
 # The same counters for the combine kernel of the GEMM workloads (one
-# iteration before the last; a product with a tail launch lists both
-# launches), plus the matrix-core counters of that kernel: bf16 MFMA busy
+# iteration before the last, on the tiles those iterations use; a product
+# with a tail launch lists both launches), plus the matrix-core counters of that kernel: bf16 MFMA busy
 # cycles over the active cycles of the 1024 SIMDs (GRBM_GUI_ACTIVE summed
 # over the 8 XCDs, divided by 8), and the clock those active cycles imply.
 # Valid only for the GEMM and planner sources they were taken on; figures
@@ -54,13 +54,13 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 GEMM_SOURCES = ("dimuon_newton_schulz_amd/csrc/gemm_kernels.hip", "dimuon_newton_schulz_amd/csrc/api.hip",
                 "dimuon_newton_schulz_amd/csrc/common.h")
 MEASURED_GEMM = {
-    "sources_sha256": "ba38b434016bbb3bdd4174eae5c675acf9be8e04d8882a61d0adf1cbedde5dfe",
+    "sources_sha256": "7b9021276e7ca79c309b6ffa87bc60999c8c7df0db0b84ea170ad2885c34c4fa",
     "gpt2_small_12x4_bf16": {"fetch_kib": [134169.8, 5246.8], "write_kib": [163840.0, 2048.0],
                              "mfma_busy_frac": 0.359, "clock_ghz": 2.19},
     "square_8x4096x4096_bf16": {"fetch_kib": [786680.8], "write_kib": [262144.0],
                                 "mfma_busy_frac": 0.539, "clock_ghz": 1.92},
-    "moe_64x(2048x1408+1408x2048)_bf16": {"fetch_kib": [1467868.3], "write_kib": [720896.0],
-                                          "mfma_busy_frac": 0.376, "clock_ghz": 1.96},
+    "moe_64x(2048x1408+1408x2048)_bf16": {"fetch_kib": [991409.2], "write_kib": [786432.4],
+                                          "mfma_busy_frac": 0.455, "clock_ghz": 2.02},
 }
 
 
