@@ -374,7 +374,7 @@ def cpu_baseline(wl_host, full_count, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(matrices are independent and would shard by ownership across GPUs)", file=sys.stderr)
         sys.exit(2)
     import torch
