@@ -71,7 +71,7 @@ struct Plan {
   // GEMM tile lists, one launch each; bm x bn tiles (symmetric products: square)
   struct GemmList { int bm, bn; std::vector<Tile> tiles; size_t off; };
   std::vector<GemmList> syrk, comb;
-  // Combine lists of the iterations before the last (empty: same as comb),
+  // Combine lists of the product iterations (empty: same as comb),
   // and the rows each matrix's iterates and B carry (KP, or KP rounded up to
   // 256 when comb_mid runs it on 256-row tiles).
   std::vector<GemmList> comb_mid;
@@ -311,13 +311,13 @@ void plan_gemm_tiles(Plan& p, bool bf16) {
       }
     }
   }
-  // Iterations before the last: a matrix whose padded Gram side is an odd
-  // multiple of 128 (at least 1024) runs the combine on 256 x 256 tiles over
-  // its rows rounded up to 256.  B and the iterates then carry 128 rows more;
-  // those rows of X' are written but never read (the Gram reads rows below
-  // KP, and so does the combine as its k operand), so they need no clearing.
-  // The last iteration keeps the lists above: Z, the norm partials and the
-  // padding of the result are those of the exact Gram side.
+  // A matrix whose padded Gram side is an odd multiple of 128 (at least
+  // 1024) runs the combine on 256 x 256 tiles over its rows rounded up to
+  // 256.  B and the iterates then carry 128 rows more; those rows of X' are
+  // written but never read (the Gram reads rows below KP, and so does the
+  // combine as its k operand), so they need no clearing, and the last
+  // iteration's combine neither stores nor sums them.  The zero-iteration
+  // combine (X read, no product) keeps the lists above.
   p.comb_mid.clear();
   p.rows.assign(p.desc.size(), 0);
   for (uint16_t i : p.gen) p.rows[i] = p.desc[i].KP;
@@ -641,7 +641,7 @@ muon_status_t launch_all(const Plan& p, const StepArgs& a, const Coeffs* cf, int
         MUON_LAUNCH(MUON_LAUNCH_GRAM, launch_syrk(a, tl(l.off), nt(l), l.bm, 0, src, first, cf[t], s));
       for (const auto& l : p.syrk)
         MUON_LAUNCH(MUON_LAUNCH_POLY, launch_syrk(a, tl(l.off), nt(l), l.bm, 1, src, first, cf[t], s));
-      for (const auto& l : (last || p.comb_mid.empty()) ? p.comb : p.comb_mid)
+      for (const auto& l : p.comb_mid.empty() ? p.comb : p.comb_mid)
         MUON_LAUNCH(MUON_LAUNCH_COMBINE,
                     launch_combine(a, tl(l.off), nt(l), l.bm, l.bn, src, dst, first, last, true, cf[t], s));
     }

@@ -584,7 +584,12 @@ __global__ __launch_bounds__((GemmT<BM, BN>::NT), 1) void k_combine_bf16(StepArg
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = XTERM ? alpha * (cf.a * x[e]) : alpha * v[e];
   };
+  // Tile rows at or beyond the Gram side (a tile of a list whose rows are
+  // padded to 256) hold no part of the result: on the last iteration they
+  // are neither stored nor summed.  The side is a multiple of 128, so an
+  // 8-row run lies wholly on one side of it.
   auto out_t = [&](int j, int i0, float (&v)[8], const uint4& aux) {
+    if (LAST && gi0 + i0 >= d.KP) return;
     fin(v, aux);
     if (LAST && partials) {
       float fr[8];
@@ -596,6 +601,7 @@ __global__ __launch_bounds__((GemmT<BM, BN>::NT), 1) void k_combine_bf16(StepArg
     store8(dst_t, (gj0 + j) * d.KP + gi0 + i0, odt, v);
   };
   auto out_n = [&](int i, int j0, float (&v)[8], const uint4& aux) {
+    if (LAST && gi0 + i >= d.KP) return;
     fin(v, aux);
     if (LAST && partials) {
       float fc[8];
@@ -616,12 +622,16 @@ __global__ __launch_bounds__((GemmT<BM, BN>::NT), 1) void k_combine_bf16(StepArg
     sp = block_sum<G::NW>(sp, red);
     // One pair per 128 x 128 sub-tile (a matrix's tiles may mix sizes): the
     // tile's sums go to its first sub-tile, zeros to the others.
+    // (Sub-tiles below the Gram side only: a padded tile's last rows have none.)
     if (threadIdx.x < (BM / 128) * (BN / 128)) {
       float* pz = reinterpret_cast<float*>(a.ws + d.pz_off);
       const int sa = threadIdx.x / (BN / 128), sb = threadIdx.x % (BN / 128);
-      const int idx = (t.ti * (BM / 128) + sa) * (d.NP / 128) + t.tj * (BN / 128) + sb;
-      pz[2 * idx] = threadIdx.x == 0 ? sz : 0.0f;
-      pz[2 * idx + 1] = threadIdx.x == 0 ? sp : 0.0f;
+      const int rs = t.ti * (BM / 128) + sa;
+      if (rs < d.KP / 128) {
+        const int idx = rs * (d.NP / 128) + t.tj * (BN / 128) + sb;
+        pz[2 * idx] = threadIdx.x == 0 ? sz : 0.0f;
+        pz[2 * idx + 1] = threadIdx.x == 0 ? sp : 0.0f;
+      }
     }
   }
 }
