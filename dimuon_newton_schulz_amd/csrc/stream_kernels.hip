@@ -281,10 +281,22 @@ __global__ __launch_bounds__(256) void k_prescale(StepArgs a, const Tile* __rest
       load8(src, sdt, off, sj0 + c0, n, v);
       load8(src, sdt, off, sj0 + c0 + 8, n, v + 8);
       const float rf = cond ? dr[row] : 1.0f;
+      // The thread's 16 column factors as four 16-byte loads (the factor
+      // array spans the padded extent, which the tile's columns never pass);
+      // columns at or beyond n take 1 as before.
+      float fc[16];
+      if (cond) {
+        const float4* q = reinterpret_cast<const float4*>(dc + sj0 + c0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float4 f = q[e];
+          fc[4 * e] = f.x; fc[4 * e + 1] = f.y; fc[4 * e + 2] = f.z; fc[4 * e + 3] = f.w;
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int col = sj0 + c0 + e;
-        const float cf = (cond && col < n) ? dc[col] : 1.0f;
+        const float cf = (cond && col < n) ? fc[e] : 1.0f;
         v[e] = (rf * v[e]) * cf;
       }
     } else {
