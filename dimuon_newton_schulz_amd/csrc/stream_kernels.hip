@@ -466,8 +466,17 @@ __global__ __launch_bounds__(256) void k_update(StepArgs a, const Tile* __restri
         zv[h][2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
       }
     }
+    // Column factors as two 16-byte loads (the factor array spans the padded
+    // extent, a multiple of 128 at least n); columns at or beyond n take 1.
+    float f8[8];
+    if (a.dimuon) {
+      const float4* q = reinterpret_cast<const float4*>(dc + col0);
+      const float4 f0 = q[0], f1 = q[1];
+      f8[0] = f0.x; f8[1] = f0.y; f8[2] = f0.z; f8[3] = f0.w;
+      f8[4] = f1.x; f8[5] = f1.y; f8[6] = f1.z; f8[7] = f1.w;
+    }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) cf[h][e] = (a.dimuon && col0 + e < n) ? dc[col0 + e] : 1.0f;
+    for (int e = 0; e < 8; ++e) cf[h][e] = (a.dimuon && col0 + e < n) ? f8[e] : 1.0f;
   }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
