@@ -54,7 +54,7 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 GEMM_SOURCES = ("dimuon_newton_schulz_amd/csrc/gemm_kernels.hip", "dimuon_newton_schulz_amd/csrc/api.hip",
                 "dimuon_newton_schulz_amd/csrc/common.h")
 MEASURED_GEMM = {
-    "sources_sha256": "d110d7a5a1d34b09340e0462452cf52026ab408eb5ff4e0267c2193639736731",
+    "sources_sha256": "e08ef813afd1849231c2a52aa26093e59315315747a2a79a42ab4503071e0edd",
     "gpt2_small_12x4_bf16": {"fetch_kib": [134169.8, 5246.8], "write_kib": [163840.0, 2048.0],
                              "mfma_busy_frac": 0.359, "clock_ghz": 2.19},
     "square_8x4096x4096_bf16": {"fetch_kib": [786680.8], "write_kib": [262144.0],

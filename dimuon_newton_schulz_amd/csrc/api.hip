@@ -71,10 +71,11 @@ struct Plan {
   // GEMM tile lists, one launch each; bm x bn tiles (symmetric products: square)
   struct GemmList { int bm, bn; std::vector<Tile> tiles; size_t off; };
   std::vector<GemmList> syrk, comb;
-  // Combine lists of the product iterations (empty: same as comb),
-  // and the rows each matrix's iterates and B carry (KP, or KP rounded up to
-  // 256 when comb_mid runs it on 256-row tiles).
-  std::vector<GemmList> comb_mid;
+  // Combine lists of the product iterations, with some matrices' rows padded
+  // to 256 (empty: comb serves them), and the rows each matrix's iterates
+  // and B carry (KP, or KP rounded up to 256 when comb_pad pads it).  comb
+  // itself serves the zero-iteration combine.
+  std::vector<GemmList> comb_pad;
   std::vector<int32_t> rows;
   std::vector<uint16_t> gen;
   // thin matrices grouped by padded Gram side KP; one tile (matrix, slice)
@@ -318,7 +319,7 @@ void plan_gemm_tiles(Plan& p, bool bf16) {
   // combine as its k operand), so they need no clearing, and the last
   // iteration's combine neither stores nor sums them.  The zero-iteration
   // combine (X read, no product) keeps the lists above.
-  p.comb_mid.clear();
+  p.comb_pad.clear();
   p.rows.assign(p.desc.size(), 0);
   for (uint16_t i : p.gen) p.rows[i] = p.desc[i].KP;
   bool big_comb = false;
@@ -337,9 +338,9 @@ void plan_gemm_tiles(Plan& p, bool bf16) {
         Plan::GemmList c{l.bm, l.bn, {}, 0};
         for (const Tile& t : l.tiles)
           if (p.rows[t.mat] == p.desc[t.mat].KP) c.tiles.push_back(t);
-        if (!c.tiles.empty()) p.comb_mid.push_back(std::move(c));
+        if (!c.tiles.empty()) p.comb_pad.push_back(std::move(c));
       }
-      p.comb_mid.push_back(std::move(pad));
+      p.comb_pad.push_back(std::move(pad));
     }
   }
 }
@@ -409,7 +410,7 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
   p.k3_off = take(sizeof(Tile) * p.k3.size());
   for (auto& l : p.syrk) l.off = take(sizeof(Tile) * l.tiles.size());
   for (auto& l : p.comb) l.off = take(sizeof(Tile) * l.tiles.size());
-  for (auto& l : p.comb_mid) l.off = take(sizeof(Tile) * l.tiles.size());
+  for (auto& l : p.comb_pad) l.off = take(sizeof(Tile) * l.tiles.size());
   p.k5_off = take(sizeof(Tile) * p.k5.size());
   p.cond_off = take(sizeof(Tile) * p.cond.size());
   p.gen_off = take(sizeof(uint16_t) * p.gen.size());
@@ -457,7 +458,7 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
     put(p.table, p.k3_off, p.k3);
     for (auto& l : p.syrk) put(p.table, l.off, l.tiles);
     for (auto& l : p.comb) put(p.table, l.off, l.tiles);
-    for (auto& l : p.comb_mid) put(p.table, l.off, l.tiles);
+    for (auto& l : p.comb_pad) put(p.table, l.off, l.tiles);
     put(p.table, p.k5_off, p.k5);
     put(p.table, p.cond_off, p.cond);
     put(p.table, p.gen_off, p.gen);
@@ -641,7 +642,7 @@ muon_status_t launch_all(const Plan& p, const StepArgs& a, const Coeffs* cf, int
         MUON_LAUNCH(MUON_LAUNCH_GRAM, launch_syrk(a, tl(l.off), nt(l), l.bm, 0, src, first, cf[t], s));
       for (const auto& l : p.syrk)
         MUON_LAUNCH(MUON_LAUNCH_POLY, launch_syrk(a, tl(l.off), nt(l), l.bm, 1, src, first, cf[t], s));
-      for (const auto& l : p.comb_mid.empty() ? p.comb : p.comb_mid)
+      for (const auto& l : p.comb_pad.empty() ? p.comb : p.comb_pad)
         MUON_LAUNCH(MUON_LAUNCH_COMBINE,
                     launch_combine(a, tl(l.off), nt(l), l.bm, l.bn, src, dst, first, last, true, cf[t], s));
     }
