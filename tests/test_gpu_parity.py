@@ -208,13 +208,14 @@ def test_combine_256x128_tiles(variant):
     run_case(wl, variant, cfg_of(wl), indices=[0, 3, 4, 5])
 
 
-@pytest.mark.parametrize("steps", [5, 1])
+@pytest.mark.parametrize("steps", [5, 1, 0])
 @pytest.mark.parametrize("variant", ["muon", "dimuon"])
 def test_combine_padded_rows(variant, steps):
     # Gram sides 1152 and 1408 (odd multiples of 128): the combine runs on
     # 256 x 256 tiles over rows rounded up to 256, and the last iteration
     # stores and sums only the rows below the Gram side (with one iteration,
-    # the first combine is also the last); a matrix with a small Gram side
+    # the first combine is also the last; with none, the exact-row combine
+    # reads the padded iterate buffers); a matrix with a small Gram side
     # shares the batch.
     shapes = [(1152, 2048), (2048, 1152), (1408, 1536), (300, 700)]
     wl = W.random_batch(shapes, dtype="bf16", ns_dtype="bf16", seed=21, variant=variant)
