@@ -373,6 +373,9 @@ def cpu_baseline(wl_host, full_count, seconds):
 
 def main():
     args = parse()
+    if args.gaussian_inputs and args.config != "c4":
+        print("--gaussian-inputs applies to --config c4 only", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(matrices are independent and would shard by ownership across GPUs)", file=sys.stderr)
