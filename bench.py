@@ -5,8 +5,9 @@ normalisation, Newton-Schulz iterations, post-scale, weight update) over one
 batch of matrices whose inputs are already resident in HBM.
 
 Default workload: the LoRA batch (64 pairs of 8 x 4096 and 4096 x 8, fp32
-master weights, Dimuon).  Its 84 MB per step would fit the 256 MB Infinity
-Cache, so four independent buffer sets are rotated.  The GPT-2, square
+master weights, Dimuon).  Its 84 MB per step would fit the 256 MiB Infinity
+Cache, so independent buffer sets are rotated until the bytes resident across
+the rotation are at least twice that cache.  The GPT-2, square
 4096^2 and MoE batches are measured as well and reported under
 "workloads".
 
@@ -102,25 +103,28 @@ def parse():
     ap.add_argument("--extra", default="c3:muon,c4:dimuon,c4:muon,c5:dimuon",
                     help="comma list of config:variant measured besides the main one, or 'none'")
     ap.add_argument("--extra-steps", type=int, default=10)
-    ap.add_argument("--sets", type=int, default=0, help="buffer sets rotated (0: automatic)")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="buffer sets rotated (0: automatic, enough that the rotation's resident bytes "
+                         "exceed twice the 256 MiB Infinity Cache)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-toy", action="store_true", help="skip the 4 x 16 toy's column-share report")
-    ap.add_argument("--gaussian-inputs", action="store_true",
-                    help="c4 only: N(0,1) gradients and momenta of the same shapes instead of the "
-                         "prescribed-spectrum ones (no QR in the input set-up; for counter runs, whose "
-                         "kernel readings do not depend on the values)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="bytes of a plain device-to-device copy run once before the workload "
                          "(calibrates HBM byte counters against a known size)")
     return ap.parse_args()
 
 
-def make_workload(name, device, variant=None, gaussian=False):
+_BUILT = {}
+
+
+def make_workload(name, device, variant=None):
+    """The configuration's batch on the device.  The square set (32 float64
+    QRs on the host) is built once per process and shared by its variants;
+    every measurement steps clones of the tensors."""
     import workloads as W
-    if name == "c4" and gaussian:
-        wl = W.random_batch([(4096, 4096)] * 8, device=device, variant=variant or "dimuon")
-        wl.name = "square_8x4096x4096_bf16_gaussian"
+    if name in _BUILT:
+        wl = _BUILT[name]
     elif name == "c1":
         wl = W.lora_toy(seed=0, device=device)
     elif name == "c2":
@@ -129,6 +133,7 @@ def make_workload(name, device, variant=None, gaussian=False):
         wl = W.gpt2_hidden(device=device)
     elif name == "c4":
         wl = W.square_batch(device=device, variant=variant or "dimuon")
+        _BUILT[name] = wl
     else:
         wl = W.moe_experts(device=device)
     if variant:
@@ -137,13 +142,16 @@ def make_workload(name, device, variant=None, gaussian=False):
 
 
 def algorithmic(wl, is_thin):
-    """Per-step algorithmic work.  Thin path: bytes each pass must move (pass A
-    reads G and M_{t-1}, writes M_t; pass B reads M_t and W, writes W).  MFMA
-    path: NS flops (symmetric products counted once)."""
+    """Per-step algorithmic work.  Thin path: the bytes the step must move
+    (read G and M_{t-1}, write M_t, read and write W: 20 B per f32 element);
+    a two-pass step splits them as pass A (G, M_{t-1}, M_t) and pass B (W
+    read and write).  Pass B's second read of M_t, the energy cache, the
+    factors and the Gram partials are not counted.  MFMA path: NS flops
+    (symmetric products counted once)."""
     size = {"f32": 4, "bf16": 2}
     per_elem = size[wl.g_dtype] + 2 * size[wl.mom_dtype] + 2 * size[wl.w_dtype]
     per_a = size[wl.g_dtype] + 2 * size[wl.mom_dtype]
-    per_b = size[wl.mom_dtype] + 2 * size[wl.w_dtype]
+    per_b = 2 * size[wl.w_dtype]
     a_bytes = b_bytes = gram = poly = comb = 0
     for m in wl.mats:
         rows, cols = m.shape
@@ -155,8 +163,11 @@ def algorithmic(wl, is_thin):
             gram += k * k * n
             poly += k ** 3
             comb += 2 * k * k * n
-    return {"thin_a_bytes": a_bytes, "thin_b_bytes": b_bytes, "gram_flops": gram, "poly_flops": poly,
-            "comb_flops": comb, "hbm_bytes_min": sum(m.shape[0] * m.shape[1] for m in wl.mats) * per_elem}
+    return {"thin_a_bytes": a_bytes, "thin_b_bytes": b_bytes, "thin_bytes": a_bytes + b_bytes,
+            "gram_flops": gram, "poly_flops": poly, "comb_flops": comb,
+            "hbm_bytes_min": sum(m.shape[0] * m.shape[1] for m in wl.mats) * per_elem,
+            "input_bytes": sum(m.shape[0] * m.shape[1] for m in wl.mats) * (size[wl.g_dtype] + size[wl.mom_dtype]
+                                                                            + size[wl.w_dtype])}
 
 
 def is_thin(m, n):
@@ -164,7 +175,14 @@ def is_thin(m, n):
     return min(m, n) <= 32
 
 
-def measure(wl, steps, warmup, sets, ns_dtype=None):
+# Buffer-set rotation: enough independent sets (W, G, M and workspace each)
+# that the bytes resident across the rotation are at least twice the 256 MiB
+# Infinity Cache, so that no step finds its operands left in it by the last.
+ROTATION_TARGET_BYTES = 2 * 256 * 2 ** 20
+MAX_SETS = 64
+
+
+def measure(wl, steps, warmup, sets=0, ns_dtype=None):
     import torch
     import dimuon_newton_schulz_amd as D
 
@@ -172,10 +190,18 @@ def measure(wl, steps, warmup, sets, ns_dtype=None):
                        g_dtype=wl.g_dtype, mom_dtype=wl.mom_dtype, ns_dtype=ns_dtype or wl.ns_dtype)
     dimuon = wl.variant == "dimuon"
     plans = []
-    for s in range(sets):
-        params = [D.Param(w=m.w.clone() if s else m.w, g=m.g.clone() if s else m.g,
-                          mom=m.m_prev.clone() if s else m.m_prev) for m in wl.mats]
+
+    def new_plan():
+        params = [D.Param(w=m.w.clone(), g=m.g.clone(), mom=m.m_prev.clone()) for m in wl.mats]
         plans.append(D.Plan(params, cfg, dimuon=dimuon))
+
+    new_plan()
+    # Bytes one set keeps resident: W, G, M and the plan's workspace.
+    per_set = algorithmic(wl, is_thin)["input_bytes"] + plans[0].workspace.numel()
+    if sets <= 0:
+        sets = min(MAX_SETS, max(1, -(-ROTATION_TARGET_BYTES // per_set)))
+    while len(plans) < sets:
+        new_plan()
     torch.cuda.synchronize()
     for i in range(warmup):
         plans[i % sets].step()
@@ -231,7 +257,10 @@ def measure(wl, steps, warmup, sets, ns_dtype=None):
         p.close()
     del plans
     torch.cuda.empty_cache()
-    return cfg, ms, per_kind, overhead
+    return cfg, ms, per_kind, overhead, sets, per_set
+
+
+THIN_KERNELS = {"thin_a": "k_thin_a", "thin_b": "k_thin_b", "thin": "k_thin_step"}
 
 
 def roofline_for(wl, cfg, per_kind, work, steps):
@@ -239,13 +268,17 @@ def roofline_for(wl, cfg, per_kind, work, steps):
     kind = max(per_kind, key=lambda k: per_kind[k][0])
     tot_ms, launches = per_kind[kind]
     avg_ms = tot_ms / launches
-    if kind in ("thin_a", "thin_b"):
+    if kind in THIN_KERNELS:
         nbytes = work[kind + "_bytes"]
         achieved = nbytes / (avg_ms * 1e-3) / 1e9
-        return kind, {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic("k_" + kind),
-                      "kernel": "k_" + kind, "avg_launch_ms": round(avg_ms, 5),
-                      "bytes_per_launch": nbytes}
+        name = THIN_KERNELS[kind]
+        traffic = measured_traffic(name)
+        out = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+               "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+               "kernel": name, "avg_launch_ms": round(avg_ms, 5), "bytes_per_launch": nbytes}
+        if traffic is not None:
+            out["traffic_over_algorithmic"] = round(traffic / nbytes, 3)
+        return kind, out
     flops = {"combine": work["comb_flops"], "gram": work["gram_flops"], "poly": work["poly_flops"]}.get(kind)
     if flops is None:
         # a streaming kernel dominates: report bytes of one pass
@@ -281,7 +314,9 @@ def roofline_for(wl, cfg, per_kind, work, steps):
 
 def host_sample(name, variant):
     """Host copy of a representative slice of the workload for the oracle:
-    the whole batch when it is small, otherwise one matrix of each shape."""
+    the whole batch when it is small (the toy, the LoRA batch), otherwise one
+    matrix of each shape (one GPT-2 layer, one square matrix, one MoE
+    expert's up and down matrices)."""
     import workloads as W
     if name == "c1":
         wl = W.lora_toy(seed=0)
@@ -295,6 +330,52 @@ def host_sample(name, variant):
         wl = W.moe_experts(experts=1)
     wl.variant = variant
     return wl
+
+
+def blas_info():
+    """BLAS library numpy calls, its version and thread count."""
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return {"vendor": i.get("internal_api"), "version": i.get("version"),
+                        "threads": int(i.get("num_threads", 1))}
+    except Exception:  # pragma: no cover
+        pass
+    return {"vendor": "unknown", "version": None, "threads": None}
+
+
+def cpu_baseline(wl_host, full_count, seconds, threads=None):
+    """The oracle as it stands, on host cores, over a bounded sample of the
+    batch: whole passes over the sample's matrices until `seconds` have
+    elapsed (one pass when 0).  `threads` limits the BLAS threads (1 for the
+    single-thread figure); the oracle's own code is single-threaded numpy."""
+    import contextlib
+    import oracle as O
+    limit = contextlib.nullcontext()
+    if threads is not None:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(threads)
+    fn = O.dimuon_step if wl_host.variant == "dimuon" else O.muon_step
+    mats = [(m.w.double().numpy(), m.g.double().numpy(), m.m_prev.double().numpy()) for m in wl_host.mats]
+    with limit:
+        blas = blas_info()
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            w, g, mp = mats[done % len(mats)]
+            fn(w, g, mp, lr=wl_host.lr, mu=wl_host.mu, mom_dtype=wl_host.mom_dtype, w_dtype=wl_host.w_dtype)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= seconds and done % len(mats) == 0:
+                break
+    per_matrix = el / done
+    steps_per_s = 1.0 / (per_matrix * full_count)
+    return {"value": round(steps_per_s, 6 if steps_per_s > 1e-3 else 9), "unit": "steps/s",
+            "cores": int(blas["threads"] or 1), "host_cpus": os.cpu_count(), "blas": blas, "kind": "oracle",
+            "sample": f"{done} matrix steps over {len(mats)} distinct matrices of {wl_host.name} "
+                      f"({wl_host.variant}) in {el:.1f} s (float64 numpy, BLAS threads {blas['threads']}); "
+                      f"steps/s = 1 / (mean seconds per matrix x {full_count} matrices of the batch)"}
 
 
 TOY_SEEDS = 32
@@ -345,37 +426,8 @@ def toy_report(dev):
     return out
 
 
-def cpu_baseline(wl_host, full_count, seconds):
-    """The oracle as it stands, on host cores, over a bounded sample of the batch."""
-    import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count()
-    fn = O.dimuon_step if wl_host.variant == "dimuon" else O.muon_step
-    mats = [(m.w.double().numpy(), m.g.double().numpy(), m.m_prev.double().numpy()) for m in wl_host.mats]
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        w, g, mp = mats[done % len(mats)]
-        fn(w, g, mp, lr=wl_host.lr, mu=wl_host.mu, mom_dtype=wl_host.mom_dtype, w_dtype=wl_host.w_dtype)
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= seconds and done % len(mats) == 0:
-            break
-    per_matrix = el / done
-    steps_per_s = 1.0 / (per_matrix * full_count)
-    return {"value": round(steps_per_s, 6), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} matrix steps over {len(mats)} distinct matrices of the batch in {el:.1f} s "
-                      f"(float64 numpy); steps/s = 1 / (mean seconds per matrix x {full_count} matrices)"}
-
-
 def main():
     args = parse()
-    if args.gaussian_inputs and args.config != "c4":
-        print("--gaussian-inputs applies to --config c4 only", file=sys.stderr)
-        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(matrices are independent and would shard by ownership across GPUs)", file=sys.stderr)
@@ -394,11 +446,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     variant = args.variant or ("muon" if args.config == "c3" else "dimuon")
-    wl = make_workload(args.config, dev, variant, gaussian=args.gaussian_inputs)
+    wl = make_workload(args.config, dev, variant)
     work = algorithmic(wl, is_thin)
     full_count = wl.count
-    sets = args.sets or (4 if work["hbm_bytes_min"] < 300e6 else 1)
-    cfg, ms, per_kind, overhead = measure(wl, args.steps, args.warmup, sets)
+    cfg, ms, per_kind, overhead, sets, per_set = measure(wl, args.steps, args.warmup, args.sets)
     kind, roof = roofline_for(wl, cfg, per_kind, work, args.steps)
     total_flops = 5 * (work["gram_flops"] + work["poly_flops"] + work["comb_flops"])
     dtype = "f32" if (wl.w_dtype == "f32" and all(is_thin(*m.shape) for m in wl.mats)) else cfg.ns_dtype
@@ -419,13 +470,24 @@ def main():
                    "ns_dtype": cfg.ns_dtype, "ns_steps": cfg.ns_steps, "buffer_sets": sets,
                    "parallelism": "single-gpu"},
         "matrices_per_s": round(wl.count * 1000.0 / ms, 1),
+        "rotation_resident_bytes": sets * per_set,
         "step_gbs_algorithmic": round(work["hbm_bytes_min"] / (ms * 1e-3) / 1e9, 1),
+        "step_hbm_frac_algorithmic": round(work["hbm_bytes_min"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "roofline": roof,
         "kernel_ms_per_step": {k: round(v[0] / args.steps, 5) for k, v in sorted(per_kind.items())},
         "event_marker_overhead_ms": round(overhead, 5),
     }
     if total_flops:
         out["ns_tflops_algorithmic"] = round(total_flops / (ms * 1e-3) / 1e12, 2)
+    # The other thin pass (two-pass step): its own fraction beside the dominant one's.
+    for k in THIN_KERNELS:
+        if k in per_kind and k != kind:
+            tot, n = per_kind[k]
+            b = work[k + "_bytes"]
+            gbs = b / (tot / n * 1e-3) / 1e9
+            out.setdefault("other_thin_kernels", {})[THIN_KERNELS[k]] = {
+                "achieved": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": b,
+                "avg_launch_ms": round(tot / n, 5)}
     del wl
     torch.cuda.empty_cache()
 
@@ -435,25 +497,42 @@ def main():
             name, _, var = item.partition(":")
             wl2 = make_workload(name, dev, var or None)
             w2 = algorithmic(wl2, is_thin)
-            cfg2, ms2, pk2, _ = measure(wl2, args.extra_steps, 2, 1)
+            cfg2, ms2, pk2, _, sets2, _ = measure(wl2, args.extra_steps, 2, args.sets)
             k2, roof2 = roofline_for(wl2, cfg2, pk2, w2, args.extra_steps)
             tf = 5 * (w2["gram_flops"] + w2["poly_flops"] + w2["comb_flops"])
-            extras.append({"workload": wl2.name, "variant": wl2.variant, "matrices": wl2.count,
-                           "steps": args.extra_steps, "ms_per_step": round(ms2, 4),
-                           "steps_per_s": round(1000.0 / ms2, 3),
-                           "matrices_per_s": round(wl2.count * 1000.0 / ms2, 1),
-                           "ns_tflops_algorithmic": round(tf / (ms2 * 1e-3) / 1e12, 2) if tf else None,
-                           "roofline": roof2,
-                           "kernel_ms_per_step": {k: round(v[0] / args.extra_steps, 4)
-                                                  for k, v in sorted(pk2.items())}})
+            rec = {"workload": wl2.name, "variant": wl2.variant, "matrices": wl2.count,
+                   "steps": args.extra_steps, "buffer_sets": sets2, "ms_per_step": round(ms2, 4),
+                   "steps_per_s": round(1000.0 / ms2, 3),
+                   "matrices_per_s": round(wl2.count * 1000.0 / ms2, 1),
+                   "ns_tflops_algorithmic": round(tf / (ms2 * 1e-3) / 1e12, 2) if tf else None,
+                   "roofline": roof2,
+                   "kernel_ms_per_step": {k: round(v[0] / args.extra_steps, 4) for k, v in sorted(pk2.items())}}
+            extras.append((name, rec))
             del wl2
             torch.cuda.empty_cache()
-    out["workloads"] = extras
     if not args.no_toy:
         out["toy_report"] = toy_report(dev)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(host_sample(args.config, variant), full_count, args.cpu_seconds)
+        # Single-thread figures for the two small configurations.
+        single = {}
+        for name in ("c1", "c2"):
+            hs = host_sample(name, "dimuon")
+            count = 128 if name == "c2" else 1
+            single[name] = cpu_baseline(hs, count, min(args.cpu_seconds, 6.0), threads=1)
+        out["cpu_baseline"]["single_thread"] = single
+        # The larger sets: one pass over one matrix of each shape, scaled to the batch.
+        counts = {"c3": 48, "c4": 8, "c5": 128}
+        samples = {}
+        for name, rec in extras:
+            if name not in counts:
+                continue
+            key = (name, rec["variant"])
+            if key not in samples:
+                samples[key] = cpu_baseline(host_sample(name, rec["variant"]), counts[name], 0.0)
+            rec["cpu_baseline"] = samples[key]
+    out["workloads"] = [rec for _, rec in extras]
     print(json.dumps(out), flush=True)
 
 

@@ -11,10 +11,23 @@ import torch
 
 import oracle as O
 
-# Tolerances: bf16 NS products -> max |O_gpu - O_ref| <= 2e-2 at the
-# orthogonaliser's output scale; fp32 NS -> ||O_gpu - O_ref||_F <= 1e-5 ||O_ref||_F.
+# Tolerances (north star of the method's step, read as stated):
+#   bf16 NS products: max |O_gpu - O_ref| <= 2e-2 on O itself (o_out: the
+#     step before the learning rate; for Dimuon after the post-scale and the
+#     norm fix), for Muon and Dimuon alike;
+#   fp32 NS products: ||O_gpu - O_ref||_F <= 1e-5 ||O_ref||_F.
+# The Dimuon norm fix ("the norm is fixed afterwards") is pinned separately:
+#   | ||O_gpu||_F / ||O_ref||_F - 1 | <= TOL_NORM_BF16 (bf16) or TOL_F32_REL
+#   (fp32).  A CPU emulation of the bf16 path's rounding points puts this
+#   ratio within 5e-4 typically and 5.1e-3 at worst (Gram side 33) on the
+#   test shapes; an error in the norm-fix constant shows up in it one to one.
 TOL_BF16_MAXABS = 2e-2
+TOL_NORM_BF16 = 1e-2
 TOL_F32_REL = 1e-5
+
+# Every comparison made in this process: (case, metric values), reported at
+# the end of the pytest session (tests/conftest.py).
+RECORDS: List[dict] = []
 
 
 def f32(x: float) -> float:
@@ -93,27 +106,42 @@ def _post_scale(ref) -> float:
 
 def check_matrix(gpu: GpuResult, ref, i: int, cfg, variant: str, wl, scale: float = 1.0,
                  o_tol: Optional[float] = None):
-    """Element-by-element comparison of matrix i; raises AssertionError with context."""
+    """Element-by-element comparison of matrix i; raises AssertionError with context.
+
+    Returns the asserted O metric: max |dO| (bf16 NS) or the relative
+    Frobenius error (fp32 NS)."""
     ctx = f"matrix {i} shape {wl.mats[i].shape} ({variant}, ns {cfg.ns_dtype})"
     o_g, o_r = gpu.o[i], ref.o
     assert np.all(np.isfinite(o_g)), f"{ctx}: non-finite O"
+    n_ref = float(np.linalg.norm(o_r))
+    n_gpu = float(np.linalg.norm(o_g))
+    norm_ratio = (n_gpu / n_ref - 1.0) if n_ref > 0 else (0.0 if n_gpu == 0 else np.inf)
+    raw = float(np.max(np.abs(o_g - o_r))) if o_g.size else 0.0
+    rel = float(np.linalg.norm(o_g - o_r) / n_ref) if n_ref > 0 else float(np.linalg.norm(o_g))
+    rec = {"case": f"{wl.name} {ctx}", "max_abs_dO": raw, "rel_F_dO": rel, "norm_ratio_m1": norm_ratio,
+           "max_abs_O": float(np.max(np.abs(o_r))) if o_r.size else 0.0}
     if cfg.ns_dtype == "bf16":
-        # Max-abs at the orthogonaliser's output scale.  For Dimuon the
-        # diagonal post-scale and the norm fix are divided out (with the
-        # oracle's factors), so the bound applies to the orthogonalised
-        # matrix itself rather than to errors the factors (up to 100x) amplify.
-        scale_out = 1.0
         if variant == "dimuon":
-            scale_out = _post_scale(ref) * ref.d_r[:, None] * ref.d_c[None, :]
-        err = np.max(np.abs(o_g - o_r) / scale_out)
+            # Diagnostic only: the error with the oracle's post-scale s and
+            # diagonal factors divided out (the orthogonaliser's own error).
+            rec["div_dO"] = float(np.max(np.abs(o_g - o_r) / (_post_scale(ref) * ref.d_r[:, None]
+                                                                 * ref.d_c[None, :])))
         tol = TOL_BF16_MAXABS if o_tol is None else o_tol
-        print(f"[parity] {ctx}: max|dO| = {err:.3e} (tol {tol})", flush=True)
-        assert err <= tol, f"{ctx}: max|dO| = {err:.3e} > {tol}"
+        RECORDS.append(rec)
+        print(f"[parity] {ctx}: max|dO| = {raw:.3e} (tol {tol}), ||O|| ratio - 1 = {norm_ratio:+.2e} "
+              f"(tol {TOL_NORM_BF16}), rel ||dO|| = {rel:.2e}"
+              + (f", divided-out max|dO| = {rec['div_dO']:.2e}" if "div_dO" in rec else ""), flush=True)
+        assert raw <= tol, f"{ctx}: max|dO| = {raw:.3e} > {tol}"
+        assert abs(norm_ratio) <= TOL_NORM_BF16, f"{ctx}: ||O_gpu|| / ||O_ref|| - 1 = {norm_ratio:.3e}"
+        err = raw
     else:
-        err = np.linalg.norm(o_g - o_r) / max(np.linalg.norm(o_r), 1e-300)
         tol = TOL_F32_REL if o_tol is None else o_tol
-        print(f"[parity] {ctx}: rel ||dO|| = {err:.3e} (tol {tol})", flush=True)
-        assert err <= tol, f"{ctx}: rel ||dO|| = {err:.3e} > {tol}"
+        RECORDS.append(rec)
+        print(f"[parity] {ctx}: rel ||dO|| = {rel:.3e} (tol {tol}), ||O|| ratio - 1 = {norm_ratio:+.2e}",
+              flush=True)
+        assert rel <= tol, f"{ctx}: rel ||dO|| = {rel:.3e} > {tol}"
+        assert abs(norm_ratio) <= tol, f"{ctx}: ||O_gpu|| / ||O_ref|| - 1 = {norm_ratio:.3e}"
+        err = rel
     # Momentum: the correctly rounded value of mu * M_prev + G, bit for bit.
     np.testing.assert_array_equal(gpu.m[i], ref.m, err_msg=f"{ctx}: momentum")
     # Weights: the update applied to the GPU's own O.  Bound: 1 ulp of the W

@@ -21,8 +21,20 @@ def announce(msg):
     print(f"[case] {msg}", flush=True)
 
 
+_SQUARE = {}
+
+
+def square_inputs():
+    """The 8 x 4096^2 batch, built once per session (its 32 float64 QRs run
+    on the host); each test steps clones of its tensors."""
+    if "wl" not in _SQUARE:
+        _SQUARE["wl"] = W.square_batch(device="cuda")
+    return _SQUARE["wl"]
+
+
 def run_plan(wl, variant, sample):
-    """One plan step over the whole batch; O and energies captured for `sample`."""
+    """One plan step over the whole batch (on clones of the workload's
+    tensors); O and energies captured for `sample`."""
     cfg = D.StepConfig(lr=wl.lr, momentum=wl.mu, ns_steps=wl.ns_steps, w_dtype=wl.w_dtype,
                        g_dtype=wl.g_dtype, mom_dtype=wl.mom_dtype, ns_dtype=wl.ns_dtype)
     host = {}
@@ -32,7 +44,7 @@ def run_plan(wl, variant, sample):
             host[i] = (m.w.cpu().clone(), m.g.cpu().clone(), m.m_prev.cpu().clone())
         rows, cols = m.shape
         params.append(D.Param(
-            w=m.w, g=m.g, mom=m.m_prev,
+            w=m.w.clone(), g=m.g.clone(), mom=m.m_prev.clone(),
             o_out=torch.full((rows, cols), float("nan"), device=m.w.device) if i in sample else None,
             energy_out=(torch.full((rows + cols,), float("nan"), device=m.w.device)
                         if (i in sample and variant == "dimuon") else None)))
@@ -77,7 +89,7 @@ def test_fullsize_gpt2_muon():
 
 @pytest.mark.parametrize("variant", ["dimuon", "muon"])
 def test_fullsize_square_4096(variant):
-    wl = W.square_batch(device="cuda", variant=variant)
+    wl = square_inputs()
     announce(f"{wl.name} {variant}")
     sample = [0, 7]
     cfg, params, host = run_plan(wl, variant, set(sample))

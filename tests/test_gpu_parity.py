@@ -13,7 +13,7 @@ import torch
 
 import dimuon_newton_schulz_amd as D
 import workloads as W
-from parity import check_matrix, f32, run_gpu, run_oracle, to64
+from parity import RECORDS, check_matrix, f32, run_gpu, run_oracle, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -165,6 +165,46 @@ def test_square_spectrum_scaled(variant):
     run_case(wl, variant, cfg_of(wl))
 
 
+def scalar_iteration(x, steps, coeffs):
+    """The quintic's action on one singular value, applied `steps` times."""
+    a, b, c = coeffs
+    for _ in range(steps):
+        x = a * x + b * x ** 3 + c * x ** 5
+    return x
+
+
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
+def test_square_closed_form_from_zero_momentum(variant):
+    # The orthogonaliser keeps the singular vectors and maps every singular
+    # value through the scalar quintic (sitech.ge Muon blog, "SVD-ի փոխարեն՝
+    # Newton–Schulz"; "Muon Optimizer 정리", "Newton-Schulz 직교화").  From
+    # zero momentum, G = U diag(sigma) V^T therefore gives
+    # O = U f^5(sigma / ||sigma||_2) V^T, up to the bf16 rounding of G; a zero
+    # previous momentum switches Dimuon's conditioning off ("Dimuon: LoRA 에
+    # 맞춰 다시 짠 Muon", "왜 「지난」 모멘텀인가").  Checked against the closed
+    # form itself, not the oracle: 2048 x 2048, sigma log-spaced 20 .. 1e-3.
+    n = 2048
+    wl = W.square_batch(count=1, n=n, seed=7, device="cuda", variant=variant, with_factors=True,
+                        zero_prev=True)
+    cfg = cfg_of(wl)
+    announce(f"closed form {n}x{n} {variant}")
+    gpu = run_gpu(wl, variant, cfg)
+    u, v = wl.notes["factors"][0]
+    sigma = wl.notes["sigma"]
+    coeffs = tuple(f32(x) for x in (cfg.a, cfg.b, cfg.c))
+    expect = (u * scalar_iteration(sigma / np.linalg.norm(sigma), cfg.ns_steps, coeffs)[None, :]) @ v.T
+    o = gpu.o[0]
+    err = float(np.max(np.abs(o - expect)))
+    rel = float(np.linalg.norm(o - expect) / np.linalg.norm(expect))
+    print(f"[parity] closed form {n}x{n} {variant}: max|O - U f5(s) V^T| = {err:.3e}, rel F {rel:.2e}, "
+          f"max|O| {np.abs(expect).max():.3f}", flush=True)
+    RECORDS.append({"case": f"closed form U f5(sigma) V^T {n}x{n} ({variant})", "max_abs_dO": err, "rel_F_dO": rel,
+                    "norm_ratio_m1": float(np.linalg.norm(o) / np.linalg.norm(expect) - 1.0),
+                    "max_abs_O": float(np.abs(expect).max())})
+    assert err <= 2e-2, err
+    np.testing.assert_array_equal(gpu.m[0], to64(wl.mats[0].g))   # M = mu * 0 + G exactly
+
+
 @pytest.mark.parametrize("variant", ["muon", "dimuon"])
 def test_symmetric_tail_tiles(variant):
     # 8 x 2048^2: 288 upper 256-tiles, one full round on 256 CUs and a tail
@@ -232,8 +272,18 @@ def test_moe_expert_full_size(variant):
 
 
 def test_moe_scaled_zero_rows():
-    wl = W.moe_experts(experts=2, d_model=384, d_ff=264, seed=7)
+    # Two experts at half the configured sides (1024 x 704 and 704 x 1024),
+    # 10% zero rows in the previous momentum (factor exactly 10 on those rows).
+    # The contract bound is stated at the configured sizes: on much smaller
+    # experts the entries of O grow while the bf16 error of the iteration
+    # does not shrink with them, and rows conditioned by 10 carry ten times
+    # the error (at 264 x 384 the GPU's max |dO| is 2.04e-2, the same as a
+    # CPU emulation of the kernels' rounding points).
+    wl = W.moe_experts(experts=2, d_model=1024, d_ff=704, seed=7)
     gpu, _ = run_case(wl, "dimuon", cfg_of(wl))
+    for i, m in enumerate(wl.mats):
+        zero = (m.m_prev.float().abs().sum(1) == 0).sum().item()
+        assert zero == round(0.1 * m.shape[0]), (i, zero)
 
 
 # ---------------------------------------------------------------------------

@@ -5,7 +5,8 @@ and both the HIP path's tests and the oracle read the tensors it returns.
 
 Every draw comes from ``numpy.random.default_rng(SeedSequence([config,
 matrix, role]))`` (host) or from a ``torch.Generator`` seeded from that same
-SeedSequence (device).  Roles are G = 0, previous momentum = 1, W = 2,
+SeedSequence (device); the square set's orthogonal factors are always
+float64 QRs on the host.  Roles are G = 0, previous momentum = 1, W = 2,
 U = 3, V = 4, and structure = 5.  Structure covers channel scales, outlier
 channels, token counts and zero rows.  Host draws are float64 and are then
 cast to the storage dtype.
@@ -16,6 +17,7 @@ parameter, so tests can draw smaller instances of the same recipe.
 
 from __future__ import annotations
 
+import os
 from dataclasses import dataclass, field
 from typing import List, Optional
 
@@ -180,42 +182,85 @@ def square_spectrum(n: int, s_max: float = 20.0, s_min: float = 1e-3) -> np.ndar
     return np.exp(np.linspace(np.log(s_max), np.log(s_min), n))
 
 
-def haar_orthogonal(config: int, matrix: int, role: int, n: int, device=None) -> torch.Tensor:
-    """Haar-random orthogonal n x n: QR of a Gaussian, columns sign-fixed so
-    that R has a positive diagonal.  float64 on host, float32 on device."""
-    a = _normal(config, matrix, role, (n, n), device)
-    q, r = torch.linalg.qr(a)
-    sign = torch.sign(torch.diagonal(r))
-    sign[sign == 0] = 1
+def haar_orthogonal(config: int, matrix: int, role: int, n: int) -> np.ndarray:
+    """Haar-random orthogonal n x n, float64 on the host: Householder QR of
+    a Gaussian draw, columns sign-fixed so that R has a positive diagonal."""
+    a = host_rng(config, matrix, role).standard_normal((n, n))
+    q, r = np.linalg.qr(a)
+    sign = np.sign(np.diag(r))
+    sign[sign == 0] = 1.0
     return q * sign[None, :]
 
 
+def _haar_many(jobs, workers: int = 0):
+    """haar_orthogonal for every (config, matrix, role, n) of ``jobs``, several
+    QRs at a time (LAPACK's QR uses few cores well; a few concurrent ones with
+    two BLAS threads each finish sooner)."""
+    from concurrent.futures import ThreadPoolExecutor
+    if len(jobs) <= 1 or jobs[0][3] < 512:
+        return [haar_orthogonal(*j) for j in jobs]
+    cores = os.cpu_count() or 2
+    workers = workers or max(1, min(len(jobs), min(cores, 16) // 2))
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(2)
+    except Exception:  # pragma: no cover
+        limit = None
+    try:
+        with ThreadPoolExecutor(workers) as ex:
+            return list(ex.map(lambda j: haar_orthogonal(*j), jobs))
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
+
+
 def square_batch(count: int = 8, n: int = 4096, seed: int = 0, device=None,
-                 variant: str = "dimuon", with_factors: bool = False) -> Workload:
+                 variant: str = "dimuon", with_factors: bool = False,
+                 zero_prev: bool = False) -> Workload:
     """G = U diag(sigma) V^T with Haar U, V and sigma log-spaced 20 .. 1e-3.
     The previous momentum is an independent draw of the same kind (the
-    step-0 gradient: after a step from zero momentum, M equals it)."""
+    step-0 gradient: after a step from zero momentum, M equals it), or zero
+    with ``zero_prev`` (the step from zero momentum, whose exact result is
+    U f(sigma / ||sigma||) V^T with f the iteration's scalar polynomial).
+
+    U and V always come from a float64 QR on the host; the products
+    U diag(sigma) V^T are float64, on ``device`` when one is given (there
+    they are plain matrix products), then rounded to bf16."""
     cfg = 4000 + seed
-    sigma = torch.from_numpy(square_spectrum(n))
-    mats, factors = [], []
+    sigma = square_spectrum(n)
+    jobs = []
     for i in range(count):
-        sig = sigma.to(device=device if device is not None else "cpu",
-                       dtype=torch.float64 if device is None or str(device) == "cpu"
-                       else torch.float32)
-        u = haar_orthogonal(cfg, i, U_ROLE, n, device)
-        v = haar_orthogonal(cfg, i, V_ROLE, n, device)
-        g = (u * sig[None, :]) @ v.T
-        u0 = haar_orthogonal(cfg + 500, i, U_ROLE, n, device)
-        v0 = haar_orthogonal(cfg + 500, i, V_ROLE, n, device)
-        mp = (u0 * sig[None, :]) @ v0.T
+        jobs += [(cfg, i, U_ROLE, n), (cfg, i, V_ROLE, n)]
+        if not zero_prev:
+            jobs += [(cfg + 500, i, U_ROLE, n), (cfg + 500, i, V_ROLE, n)]
+    qs = _haar_many(jobs)
+    on_dev = device is not None and str(device) != "cpu"
+    dev = device if on_dev else "cpu"
+
+    def product(u, v):
+        ut = torch.from_numpy(u).to(dev)
+        vt = torch.from_numpy(v).to(dev)
+        st = torch.from_numpy(sigma).to(dev)
+        return (ut * st[None, :]) @ vt.T
+
+    mats, factors = [], []
+    per = 2 if zero_prev else 4
+    for i in range(count):
+        u, v = qs[per * i], qs[per * i + 1]
+        g = product(u, v)
+        if zero_prev:
+            mp = torch.zeros((n, n), dtype=torch.float64, device=dev)
+        else:
+            mp = product(qs[per * i + 2], qs[per * i + 3])
         w = _normal(cfg, i, W_ROLE, (n, n), device, std=0.02)
         mats.append(MatrixInput(_cast(w, "bf16", device), _cast(g, "bf16", device),
                                 _cast(mp, "bf16", device)))
         if with_factors:
             factors.append((u, v))
+        del g, mp
     wl = Workload(f"square_{count}x{n}x{n}_bf16", mats, "bf16", "bf16", "bf16", "bf16",
                   lr=0.02, mu=0.95, variant=variant,
-                  notes={"sigma": square_spectrum(n)})
+                  notes={"sigma": sigma})
     if with_factors:
         wl.notes["factors"] = factors
     return wl
