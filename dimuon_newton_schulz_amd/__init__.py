@@ -224,19 +224,34 @@ def workspace_for(params: Sequence[Param], cfg: StepConfig, device=None) -> torc
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
 
 
+def _torch_stream(stream, device):
+    """The launch stream as a torch stream object (None: the current stream)."""
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if hasattr(stream, "cuda_stream"):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
 def _step(fn_name: str, params: Sequence[Param], cfg: StepConfig, workspace: Optional[torch.Tensor],
           stream=None):
     lib = load_library()
     _check_dtypes(params, cfg)
     arr = _marshal(params)
     c, _keep = cfg.to_c()
+    device = params[0].w.device
+    ts = _torch_stream(stream, device)
     if workspace is None:
         workspace = workspace_for(params, cfg)
-    handle = _stream_handle(stream, params[0].w.device)
+        # Allocated on the current stream; if the kernels run on another one,
+        # the caching allocator must not hand the block out again before they
+        # finish.
+        if ts != torch.cuda.current_stream(device):
+            workspace.record_stream(ts)
     fn = getattr(lib, fn_name)
-    with torch.cuda.device(params[0].w.device):
+    with torch.cuda.device(device):
         _check(fn(arr, len(params), ctypes.byref(c), ctypes.c_void_p(workspace.data_ptr()),
-                  ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(handle)))
+                  ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(ts.cuda_stream)))
     return workspace
 
 

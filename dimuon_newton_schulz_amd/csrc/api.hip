@@ -478,6 +478,13 @@ struct Staging {
   hipEvent_t ev = nullptr;
   bool pending = false;
 
+  // True when the buffer may be written: no copy from it is in flight.
+  bool idle() {
+    if (!pending) return true;
+    if (hipEventQuery(ev) == hipSuccess) pending = false;
+    return !pending;
+  }
+
   muon_status_t upload(const std::vector<unsigned char>& table, void* dst, hipStream_t s) {
     hipError_t err;
     if (pending) {
@@ -519,15 +526,35 @@ struct Staging {
   }
 };
 
-// Stateless calls rotate through a few staging buffers per host thread, so
-// the host can run several steps ahead of the GPU.  They live until the
-// process ends.
-constexpr int kRing = 4;
-struct StagingRing {
-  Staging slot[kRing];
-  int next = 0;
+// Staging buffers of the stateless calls, per host thread.  A call takes an
+// idle buffer (its previous copy has completed), or a new one while the
+// thread holds fewer than kPoolMax; only a thread with kPoolMax copies in
+// flight waits, for its oldest.  The buffers are freed when the thread exits.
+constexpr size_t kPoolMax = 64;
+struct StagingPool {
+  std::vector<Staging*> slots;
+  size_t oldest = 0;   // slot waited on when every slot is busy
+
+  Staging* take() {
+    for (Staging* st : slots)
+      if (st->idle()) return st;
+    if (slots.size() < kPoolMax) {
+      slots.push_back(new Staging());
+      return slots.back();
+    }
+    Staging* st = slots[oldest];
+    oldest = (oldest + 1) % slots.size();
+    return st;   // upload() waits for its copy
+  }
+
+  ~StagingPool() {
+    for (Staging* st : slots) {
+      st->release();
+      delete st;
+    }
+  }
 };
-thread_local StagingRing* g_ring = nullptr;
+thread_local StagingPool g_pool;
 
 // ---------------------------------------------------------------------------
 // Shared pieces of a step
@@ -660,10 +687,7 @@ muon_status_t run_step(const muon_matrix_t* mats, int64_t count, const muon_conf
   muon_status_t st = prepare(mats, count, cfg, ws, ws_bytes, p);
   if (st != MUON_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream_ptr);
-  if (!g_ring) g_ring = new StagingRing();
-  Staging& slot = g_ring->slot[g_ring->next];
-  g_ring->next = (g_ring->next + 1) % kRing;
-  if ((st = slot.upload(p.table, ws, s)) != MUON_OK) return st;
+  if ((st = g_pool.take()->upload(p.table, ws, s)) != MUON_OK) return st;
   Coeffs cf[kMaxSteps];
   make_coeffs(*cfg, cf);
   return launch_all(p, make_args(p, *cfg, ws, dimuon), cf, cfg->ns_steps, dimuon, 0, false, s);

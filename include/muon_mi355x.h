@@ -48,8 +48,13 @@
  *     the dtype in the config.  Device pointers must be 16-byte aligned.
  *   - The caller owns all memory, including the workspace.  The library
  *     allocates no device memory.  It does allocate pinned host staging
- *     buffers (a few per host thread, and one per plan), from which the
- *     batch's descriptor table is copied into the workspace.
+ *     buffers, from which the batch's descriptor table (a few KB per matrix
+ *     batch) is copied into the workspace: muon_step and dimuon_step keep
+ *     them per host thread, take one whose previous copy has completed or
+ *     else allocate another (hipHostMalloc), up to 64 per thread, and free
+ *     them when the thread exits; a plan holds one, freed by
+ *     muon_plan_destroy.  The only host-side wait: a thread that already
+ *     has 64 descriptor copies in flight waits for its oldest.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
  *     default stream).  Host-side validation runs before anything is
  *     enqueued.  An invalid call returns an error code and leaves every
@@ -136,7 +141,9 @@ muon_status_t muon_workspace_bytes(const muon_matrix_t* mats, int64_t count,
 
 /* One Muon step over `count` matrices (host array `mats`).  `workspace` is
  * device memory of at least muon_workspace_bytes() bytes, 256-byte aligned.
- * Enqueues on `stream` and returns without synchronising.
+ * Enqueues on `stream` and returns without synchronising (a thread with 64
+ * descriptor copies still in flight first waits for its oldest; see the
+ * staging buffers above).
  * Errors: INVALID_ARG, DTYPE, WORKSPACE, ALIAS, UNSUPPORTED, HIP. */
 muon_status_t muon_step(const muon_matrix_t* mats, int64_t count,
                         const muon_config_t* cfg, void* workspace,

@@ -171,3 +171,62 @@ def test_plan_create_rejects_invalid_batches():
     assert lib.muon_plan_step(None, None) == 1
     assert lib.muon_plan_set_lr(None, 0.1) == 1
     lib.muon_plan_destroy(None)
+
+
+def test_binding_records_workspace_on_launch_stream(monkeypatch):
+    # A workspace the binding allocates on the current stream is recorded on
+    # the launch stream when the two differ, and not otherwise (CPU: the
+    # library, the allocation and the streams are stand-ins).
+    import torch
+
+    class FakeStream:
+        def __init__(self, h):
+            self.cuda_stream = h
+
+        def __eq__(self, other):
+            return isinstance(other, FakeStream) and other.cuda_stream == self.cuda_stream
+
+        def __ne__(self, other):
+            return not self == other
+
+    class FakeWorkspace:
+        def __init__(self):
+            self.recorded = []
+
+        def record_stream(self, s):
+            self.recorded.append(s)
+
+        def data_ptr(self):
+            return 0x1000
+
+        def numel(self):
+            return 256
+
+    class FakeLib:
+        def __init__(self):
+            self.calls = []
+
+        def muon_step(self, arr, n, cfg, ws, ws_bytes, stream):
+            self.calls.append(stream.value or 0)
+            return 0
+
+    lib = FakeLib()
+    current = FakeStream(0)
+    made = []
+
+    def fake_ws(params, cfg, device=None):
+        made.append(FakeWorkspace())
+        return made[-1]
+
+    monkeypatch.setattr(D, "load_library", lambda *a, **k: lib)
+    monkeypatch.setattr(D, "workspace_for", fake_ws)
+    monkeypatch.setattr(torch.cuda, "current_stream", lambda device=None: current)
+    monkeypatch.setattr(torch.cuda, "device", lambda d: __import__("contextlib").nullcontext())
+    t = torch.zeros(8, 64, dtype=torch.bfloat16)
+    p = D.Param(w=t, g=t.clone(), mom=t.clone())
+    D.muon_step([p], D.StepConfig())
+    assert made[-1].recorded == [] and lib.calls[-1] == 0
+    side = FakeStream(77)
+    D.muon_step([p], D.StepConfig(), stream=side)
+    assert made[-1].recorded == [side] and lib.calls[-1] == 77
+
