@@ -29,7 +29,7 @@ STATUS_NAMES = {0: "MUON_OK", 1: "MUON_ERR_INVALID_ARG", 2: "MUON_ERR_DTYPE",
                 3: "MUON_ERR_WORKSPACE", 4: "MUON_ERR_ALIAS", 5: "MUON_ERR_HIP",
                 6: "MUON_ERR_UNSUPPORTED"}
 
-EXPORTED_SYMBOLS = ("muon_config_default", "muon_workspace_bytes", "muon_step", "dimuon_step",
+EXPORTED_SYMBOLS = ("muon_config_default", "muon_workspace_bytes", "muon_step", "dimuon_step", "muon_step_noalloc",
                     "muon_set_launch_events", "muon_plan_create", "muon_plan_step", "muon_plan_set_lr",
                     "muon_plan_reset", "muon_plan_destroy", "muon_status_string", "muon_last_error", "muon_abi_version")
 
@@ -83,6 +83,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.argtypes = [ctypes.POINTER(MuonMatrix), ctypes.c_int64, ctypes.POINTER(MuonConfig),
                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         fn.restype = ctypes.c_int
+    lib.muon_step_noalloc.argtypes = [ctypes.POINTER(MuonMatrix), ctypes.c_int64, ctypes.POINTER(MuonConfig),
+                                      ctypes.c_int32, ctypes.c_void_p]
+    lib.muon_step_noalloc.restype = ctypes.c_int
     lib.muon_set_launch_events.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]
     lib.muon_set_launch_events.restype = ctypes.c_int32
     lib.muon_plan_create.argtypes = [ctypes.POINTER(MuonMatrix), ctypes.c_int64, ctypes.POINTER(MuonConfig),
@@ -267,6 +270,24 @@ def dimuon_step(params: Sequence[Param], cfg: StepConfig, workspace: Optional[to
     return _step("dimuon_step", params, cfg, workspace, stream)
 
 
+NOALLOC_MAX_BYTES = 64 << 20   # MUON_NOALLOC_MAX_BYTES
+
+
+def muon_step_noalloc(params: Sequence[Param], cfg: StepConfig, dimuon: bool, stream=None) -> None:
+    """One Muon (dimuon False) or Dimuon step without a workspace argument:
+    the library's static device scratch serves (muon_step_noalloc).  Nothing
+    is allocated; calls on one GPU must be ordered (they share the scratch)."""
+    lib = load_library()
+    _check_dtypes(params, cfg)
+    arr = _marshal(params)
+    c, _keep = cfg.to_c()
+    device = params[0].w.device
+    ts = _torch_stream(stream, device)
+    with torch.cuda.device(device):
+        _check(lib.muon_step_noalloc(arr, len(params), ctypes.byref(c), 1 if dimuon else 0,
+                                     ctypes.c_void_p(ts.cuda_stream)))
+
+
 class LaunchTimer:
     """Per-launch HIP events for one step at a time (timing only).
 
@@ -355,6 +376,6 @@ class Plan:
 
 
 __all__ = ["MuonMatrix", "MuonConfig", "MuonError", "StepConfig", "Param", "load_library",
-           "muon_step", "dimuon_step", "muon_workspace_bytes", "muon_status_string",
+           "muon_step", "dimuon_step", "muon_step_noalloc", "muon_workspace_bytes", "muon_status_string",
            "Plan", "workspace_for", "config_for", "EXPORTED_SYMBOLS", "LaunchTimer",
            "LAUNCH_KINDS"]

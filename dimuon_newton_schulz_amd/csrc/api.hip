@@ -693,6 +693,86 @@ muon_status_t run_step(const muon_matrix_t* mats, int64_t count, const muon_conf
   return launch_all(p, make_args(p, *cfg, ws, dimuon), cf, cfg->ns_steps, dimuon, 0, false, s);
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free step (muon_step_noalloc): the workspace is `scratch`, a
+// static device array each GPU holds until the process ends, and the
+// descriptor table reaches it through kernel arguments, so the call needs
+// neither a device allocation nor a host staging buffer.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = MUON_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of this device's `scratch`, looked up once per device with
+// that device current.  Host code uses only this address: the array's own
+// name is a host-side stand-in, not a device address.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+muon_status_t scratch_base(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MUON_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MUON_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return fail(MUON_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MUON_OK;
+}
+
+// One piece of the descriptor table, carried by value as a kernel argument
+// (2 KB: 128 threads of 16 bytes).
+constexpr int kPieceBytes = 2048;
+struct alignas(16) TablePiece {
+  uint4 v[kPieceBytes / 16];
+};
+
+__global__ __launch_bounds__(kPieceBytes / 16) void k_put_table(uint4* dst, TablePiece piece, int n16) {
+  const int i = threadIdx.x;
+  if (i < n16) dst[i] = piece.v[i];
+}
+
+muon_status_t run_step_noalloc(const muon_matrix_t* mats, int64_t count, const muon_config_t* cfg, bool dimuon,
+                               void* stream_ptr) {
+  g_last_error.clear();
+  muon_status_t st;
+  if ((st = validate_config(cfg)) != MUON_OK) return st;
+  if ((st = validate_shapes(mats, count)) != MUON_OK) return st;
+  if ((st = validate_buffers(mats, count, cfg)) != MUON_OK) return st;
+  {
+    Plan sized;
+    if ((st = build_plan(mats, count, cfg, false, sized)) != MUON_OK) return st;
+    if (sized.total_bytes > kScratchBytes)
+      return fail(MUON_ERR_WORKSPACE, "batch needs %zu bytes of workspace, above the %zu-byte static scratch",
+                  sized.total_bytes, kScratchBytes);
+  }
+  void* base = nullptr;
+  if ((st = scratch_base(&base)) != MUON_OK) return st;
+  Plan p;
+  if ((st = prepare(mats, count, cfg, base, kScratchBytes, p)) != MUON_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream_ptr);
+  // The table, zero-padded to whole 16-byte units, piece by piece (its size
+  // is a multiple of 256 bytes).
+  const size_t n16 = p.table.size() / 16;
+  for (size_t at = 0; at < n16; at += kPieceBytes / 16) {
+    TablePiece piece;
+    const size_t cnt = std::min<size_t>(kPieceBytes / 16, n16 - at);
+    std::memset(&piece, 0, sizeof(piece));
+    std::memcpy(&piece, p.table.data() + at * 16, cnt * 16);
+    hipLaunchKernelGGL(k_put_table, dim3(1), dim3(kPieceBytes / 16), 0, s, static_cast<uint4*>(base) + at, piece,
+                       static_cast<int>(cnt));
+    MUON_HIP_TRY(hipGetLastError());
+  }
+  Coeffs cf[kMaxSteps];
+  make_coeffs(*cfg, cf);
+  return launch_all(p, make_args(p, *cfg, base, dimuon), cf, cfg->ns_steps, dimuon, 0, false, s);
+}
+
 }  // namespace
 }  // namespace muon
 
@@ -755,6 +835,11 @@ muon_status_t muon_step(const muon_matrix_t* mats, int64_t count, const muon_con
 muon_status_t dimuon_step(const muon_matrix_t* mats, int64_t count, const muon_config_t* cfg, void* workspace,
                           size_t workspace_bytes, void* stream) {
   return muon::run_step(mats, count, cfg, workspace, workspace_bytes, stream, true);
+}
+
+muon_status_t muon_step_noalloc(const muon_matrix_t* mats, int64_t count, const muon_config_t* cfg, int32_t dimuon,
+                                void* stream) {
+  return muon::run_step_noalloc(mats, count, cfg, dimuon != 0, stream);
 }
 
 int32_t muon_set_launch_events(void* const* events, int32_t* kinds, int32_t n) {

@@ -154,6 +154,31 @@ muon_status_t dimuon_step(const muon_matrix_t* mats, int64_t count,
                           const muon_config_t* cfg, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  One Muon step
+ * (dimuon = 0) or Dimuon step (dimuon != 0) with the semantics of
+ * muon_step / dimuon_step, but with no workspace argument: the library's
+ * own static device array of MUON_NOALLOC_MAX_BYTES (64 MiB, held by each
+ * GPU the library runs on until the process ends) serves as the workspace,
+ * and the descriptor table reaches it through kernel arguments.  The call
+ * allocates nothing: no device memory, no pinned host memory.
+ *   - The batch must fit: a batch whose muon_workspace_bytes() exceeds
+ *     MUON_NOALLOC_MAX_BYTES is rejected with MUON_ERR_WORKSPACE before
+ *     anything is enqueued.  (Thin batches fit easily: the 64 LoRA pairs
+ *     of 8 x 4096 and 4096 x 8 need about 7 MB.)
+ *   - `stream` must belong to the current device; the array of that device
+ *     is used.  Every call on one GPU shares that GPU's array, which keeps
+ *     the last call's contents (no call depends on them): calls that
+ *     overlap on one GPU race and must be ordered, for example on one
+ *     stream.
+ *   - Results equal muon_step / dimuon_step bit for bit (the same kernels).
+ * Errors: INVALID_ARG, DTYPE, WORKSPACE (batch too large), ALIAS,
+ * UNSUPPORTED, HIP. */
+#define MUON_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+muon_status_t muon_step_noalloc(const muon_matrix_t* mats, int64_t count,
+                                const muon_config_t* cfg, int32_t dimuon,
+                                void* stream);
+
 /* Kernel kinds reported by the launch-event hook. */
 typedef enum muon_launch_kind {
   MUON_LAUNCH_START = -1,     /* event recorded before the first launch */

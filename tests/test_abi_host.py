@@ -230,3 +230,15 @@ def test_binding_records_workspace_on_launch_stream(monkeypatch):
     D.muon_step([p], D.StepConfig(), stream=side)
     assert made[-1].recorded == [side] and lib.calls[-1] == 77
 
+
+def test_noalloc_rejects_oversized_batch_before_any_hip_call():
+    # 4096 x 4096 in bf16 needs far more than the 64 MiB static scratch; the
+    # check runs on the host before the scratch is looked up.
+    lib = D.load_library()
+    arr = _mats([(4096, 4096)])
+    cfg, _keep = _cfg()
+    st, need = _ws_bytes(arr, 1, cfg)
+    assert st == 0 and need > D.NOALLOC_MAX_BYTES
+    st = lib.muon_step_noalloc(arr, 1, ctypes.byref(cfg), 0, None)
+    assert st == 3, st
+    assert b"static scratch" in lib.muon_last_error()
