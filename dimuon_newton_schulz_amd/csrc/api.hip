@@ -649,13 +649,19 @@ muon_status_t launch_all(const Plan& p, const StepArgs& a, const Coeffs* cf, int
   }
   if (!p.gen.empty()) {
     const int ng = static_cast<int>(p.gen.size());
-    MUON_LAUNCH(MUON_LAUNCH_MOMENTUM, launch_momentum(a, tl(p.k1_off), static_cast<int>(p.k1.size()), dimuon, s));
+    const int n3 = static_cast<int>(p.k3.size());
     if (dimuon) {
+      // The factors need the energies of M_{t-1} (a reduction over whole rows
+      // and columns) before anything is scaled: momentum with the energy
+      // partials, the factors, then the prescale of M_t.
       const int nc = static_cast<int>(p.cond.size());
+      MUON_LAUNCH(MUON_LAUNCH_MOMENTUM, launch_momentum(a, tl(p.k1_off), static_cast<int>(p.k1.size()), true, s));
       MUON_LAUNCH(MUON_LAUNCH_CONDITION, launch_cond_energy(a, tl(p.cond_off), nc, s));
       MUON_LAUNCH(MUON_LAUNCH_CONDITION, launch_cond_factor(a, tl(p.cond_off), nc, s));
+      MUON_LAUNCH(MUON_LAUNCH_PRESCALE, launch_prescale(a, tl(p.k3_off), n3, false, s));
+    } else {
+      MUON_LAUNCH(MUON_LAUNCH_MOMENTUM_PRESCALE, launch_prescale(a, tl(p.k3_off), n3, true, s));
     }
-    MUON_LAUNCH(MUON_LAUNCH_PRESCALE, launch_prescale(a, tl(p.k3_off), static_cast<int>(p.k3.size()), s));
     MUON_LAUNCH(MUON_LAUNCH_NORM, launch_norm_finalize(a, il(p.gen_off), ng, s));
     auto nt = [](const Plan::GemmList& l) { return static_cast<int>(l.tiles.size()); };
     if (ns_steps == 0)

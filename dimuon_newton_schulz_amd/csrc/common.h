@@ -329,7 +329,8 @@ hipError_t launch_momentum(const StepArgs& a, const Tile* tiles, int n, bool ene
 // chunk): energies and chunk maxima, then the factors (zero in the padding).
 hipError_t launch_cond_energy(const StepArgs& a, const Tile* tiles, int n, hipStream_t s);
 hipError_t launch_cond_factor(const StepArgs& a, const Tile* tiles, int n, hipStream_t s);
-hipError_t launch_prescale(const StepArgs& a, const Tile* tiles, int n, hipStream_t s);
+// Prescale; `momentum` (Muon only): the momentum update in the same pass.
+hipError_t launch_prescale(const StepArgs& a, const Tile* tiles, int n, bool momentum, hipStream_t s);
 hipError_t launch_norm_finalize(const StepArgs& a, const uint16_t* mats, int n, hipStream_t s);
 hipError_t launch_post_finalize(const StepArgs& a, const uint16_t* mats, int n, hipStream_t s);
 hipError_t launch_update(const StepArgs& a, const Tile* tiles, int n, hipStream_t s);

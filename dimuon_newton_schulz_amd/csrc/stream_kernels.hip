@@ -252,7 +252,11 @@ __global__ __launch_bounds__(256) void k_cond_factor(StepArgs a, const Tile* __r
 // dtype, written in the Gram orientation (KP x NP) and its transpose
 // (NP x KP), zero in the padding; one ||Y||^2 partial per tile.
 // Tile: 64 x 64 of the Gram orientation; the source tile goes through LDS.
+// MOM (Muon, which needs no energies): the momentum update happens here as
+// well, M_t = mu M_{t-1} + G computed from the loaded M_{t-1} and G and
+// stored, so M_t is not read back; each element belongs to one tile.
 // ---------------------------------------------------------------------------
+template <bool MOM>
 __global__ __launch_bounds__(256) void k_prescale(StepArgs a, const Tile* __restrict__ tiles) {
   __shared__ float tileS[64][65];
   __shared__ float red[4];
@@ -263,7 +267,7 @@ __global__ __launch_bounds__(256) void k_prescale(StepArgs a, const Tile* __rest
   const bool cond = a.dimuon && a.scal[d.scal_idx].cond_on != 0.0f;
   const float* dr = reinterpret_cast<const float*>(a.ws + d.dr_off);
   const float* dc = reinterpret_cast<const float*>(a.ws + d.dc_off);
-  const bool use_v = a.nesterov && d.v_off >= 0;
+  const bool use_v = !MOM && a.nesterov && d.v_off >= 0;
   const void* src = use_v ? static_cast<const void*>(a.ws + d.v_off) : static_cast<const void*>(d.mom);
   const int sdt = use_v ? DT_F32 : a.mom_dt;
 
@@ -280,6 +284,19 @@ __global__ __launch_bounds__(256) void k_prescale(StepArgs a, const Tile* __rest
       const int64_t off = static_cast<int64_t>(row) * n;
       load8(src, sdt, off, sj0 + c0, n, v);
       load8(src, sdt, off, sj0 + c0 + 8, n, v + 8);
+      if constexpr (MOM) {
+        float gv[16];
+        load8(d.g, a.g_dt, off, sj0 + c0, n, gv);
+        load8(d.g, a.g_dt, off, sj0 + c0 + 8, n, gv + 8);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = momentum_value(a.mu, v[e], gv[e], a.mom_dt);
+        store8(d.mom, a.mom_dt, off, sj0 + c0, n, v);
+        store8(d.mom, a.mom_dt, off, sj0 + c0 + 8, n, v + 8);
+        if (a.nesterov) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) v[e] = gv[e] + a.mu * v[e];
+        }
+      }
       const float rf = cond ? dr[row] : 1.0f;
       // The thread's 16 column factors as four 16-byte loads (the factor
       // array spans the padded extent, which the tile's columns never pass);
@@ -516,9 +533,10 @@ hipError_t launch_cond_factor(const StepArgs& a, const Tile* tiles, int n, hipSt
   return hipGetLastError();
 }
 
-hipError_t launch_prescale(const StepArgs& a, const Tile* tiles, int n, hipStream_t s) {
+hipError_t launch_prescale(const StepArgs& a, const Tile* tiles, int n, bool momentum, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_prescale, dim3(n), dim3(256), 0, s, a, tiles);
+  if (momentum) hipLaunchKernelGGL(k_prescale<true>, dim3(n), dim3(256), 0, s, a, tiles);
+  else hipLaunchKernelGGL(k_prescale<false>, dim3(n), dim3(256), 0, s, a, tiles);
   return hipGetLastError();
 }
 

@@ -193,7 +193,8 @@ typedef enum muon_launch_kind {
   MUON_LAUNCH_POSTNORM = 8,   /* Dimuon norm fix */
   MUON_LAUNCH_UPDATE = 9,     /* O and the weight update */
   MUON_LAUNCH_THIN_ENERGY = 10, /* thin path: energies of M_{t-1} (no cached energies) */
-  MUON_LAUNCH_THIN_A = 11     /* thin path pass A: momentum, Gram partials */
+  MUON_LAUNCH_THIN_A = 11,    /* thin path pass A: momentum, Gram partials */
+  MUON_LAUNCH_MOMENTUM_PRESCALE = 12  /* Muon: momentum and prescale in one pass */
 } muon_launch_kind_t;
 
 /* Timing hook, per host thread; not part of the method.  When `events` is

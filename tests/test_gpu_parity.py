@@ -136,6 +136,29 @@ def test_general_ragged_mixed_batch(variant, ns):
     run_case(wl, variant, cfg_of(wl))
 
 
+@pytest.mark.parametrize("wdt", ["bf16", "f32"])
+def test_muon_streaming_passes_fused(wdt):
+    # Muon: the momentum update runs inside the prescale launch (M_t is not
+    # read back), so no separate momentum launch remains; Dimuon keeps it
+    # (its factors need the energies of M_{t-1} first).  Ragged and whole
+    # 16-byte runs, wide and tall, f32 and bf16 storage.
+    shapes = [(200, 333), (333, 200), (256, 1024), (1000, 130), (8, 512)]
+    wl = W.random_batch(shapes, dtype=wdt, ns_dtype="bf16", seed=17)
+    cfg = cfg_of(wl)
+    params = [D.Param(w=m.w.cuda().clone(), g=m.g.cuda().clone(), mom=m.m_prev.cuda().clone()) for m in wl.mats]
+    announce(f"fused streaming passes {wdt}: launch kinds")
+    kinds = launch_kinds(lambda: D.muon_step(params, cfg))
+    assert kinds.count("momentum_prescale") == 1 and kinds.count("update") == 1, kinds
+    assert not {"momentum", "prescale"} & set(kinds), kinds
+    f32 = launch_kinds(lambda: D.muon_step(params, cfg_of(wl, ns_dtype="f32")))
+    assert "momentum_prescale" in f32 and "momentum" not in f32, f32
+    dim = launch_kinds(lambda: D.dimuon_step(params, cfg))
+    assert "momentum" in dim and "prescale" in dim and "momentum_prescale" not in dim, dim
+    del params
+    run_case(wl, "muon", cfg)
+    run_case(wl, "muon", cfg_of(wl, nesterov=True, weight_decay=0.1), scales=[0.5, 2.0, 1.0, 1.5, 0.25])
+
+
 @pytest.mark.parametrize("variant", ["muon", "dimuon"])
 def test_general_f32_storage(variant):
     shapes = [(200, 333), (333, 200), (64, 1024)]
