@@ -109,6 +109,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-toy", action="store_true", help="skip the 4 x 16 toy's column-share report")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the plans replaying their launch sequences as HIP graphs")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="bytes of a plain device-to-device copy run once before the workload "
                          "(calibrates HBM byte counters against a known size)")
@@ -182,7 +184,7 @@ ROTATION_TARGET_BYTES = 2 * 256 * 2 ** 20
 MAX_SETS = 64
 
 
-def measure(wl, steps, warmup, sets=0, ns_dtype=None):
+def measure(wl, steps, warmup, sets=0, ns_dtype=None, graph=False):
     import torch
     import dimuon_newton_schulz_amd as D
 
@@ -202,8 +204,13 @@ def measure(wl, steps, warmup, sets=0, ns_dtype=None):
         sets = min(MAX_SETS, max(1, -(-ROTATION_TARGET_BYTES // per_set)))
     while len(plans) < sets:
         new_plan()
+    if graph:
+        for p in plans:
+            p.set_graph(True)
     torch.cuda.synchronize()
-    for i in range(warmup):
+    # With graphs, every plan first runs its eager step and captures both of
+    # its states before the timed region.
+    for i in range(warmup + (3 * sets if graph else 0)):
         plans[i % sets].step()
     torch.cuda.synchronize()
 
@@ -449,7 +456,7 @@ def main():
     wl = make_workload(args.config, dev, variant)
     work = algorithmic(wl, is_thin)
     full_count = wl.count
-    cfg, ms, per_kind, overhead, sets, per_set = measure(wl, args.steps, args.warmup, args.sets)
+    cfg, ms, per_kind, overhead, sets, per_set = measure(wl, args.steps, args.warmup, args.sets, graph=args.graph)
     kind, roof = roofline_for(wl, cfg, per_kind, work, args.steps)
     total_flops = 5 * (work["gram_flops"] + work["poly_flops"] + work["comb_flops"])
     dtype = "f32" if (wl.w_dtype == "f32" and all(is_thin(*m.shape) for m in wl.mats)) else cfg.ns_dtype
@@ -468,7 +475,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "variant": wl.variant, "matrices": wl.count,
                    "ns_dtype": cfg.ns_dtype, "ns_steps": cfg.ns_steps, "buffer_sets": sets,
-                   "parallelism": "single-gpu"},
+                   "launches": "hip graph" if args.graph else "stream", "parallelism": "single-gpu"},
         "matrices_per_s": round(wl.count * 1000.0 / ms, 1),
         "rotation_resident_bytes": sets * per_set,
         "step_gbs_algorithmic": round(work["hbm_bytes_min"] / (ms * 1e-3) / 1e9, 1),
@@ -497,7 +504,7 @@ def main():
             name, _, var = item.partition(":")
             wl2 = make_workload(name, dev, var or None)
             w2 = algorithmic(wl2, is_thin)
-            cfg2, ms2, pk2, _, sets2, _ = measure(wl2, args.extra_steps, 2, args.sets)
+            cfg2, ms2, pk2, _, sets2, _ = measure(wl2, args.extra_steps, 2, args.sets, graph=args.graph)
             k2, roof2 = roofline_for(wl2, cfg2, pk2, w2, args.extra_steps)
             tf = 5 * (w2["gram_flops"] + w2["poly_flops"] + w2["comb_flops"])
             rec = {"workload": wl2.name, "variant": wl2.variant, "matrices": wl2.count,

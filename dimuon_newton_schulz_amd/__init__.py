@@ -31,7 +31,7 @@ STATUS_NAMES = {0: "MUON_OK", 1: "MUON_ERR_INVALID_ARG", 2: "MUON_ERR_DTYPE",
 
 EXPORTED_SYMBOLS = ("muon_config_default", "muon_workspace_bytes", "muon_step", "dimuon_step", "muon_step_noalloc",
                     "muon_set_launch_events", "muon_plan_create", "muon_plan_step", "muon_plan_set_lr",
-                    "muon_plan_reset", "muon_plan_destroy", "muon_status_string", "muon_last_error", "muon_abi_version")
+                    "muon_plan_reset", "muon_plan_set_graph", "muon_plan_destroy", "muon_status_string", "muon_last_error", "muon_abi_version")
 
 LAUNCH_KINDS = {-1: "start", 0: "thin_b", 1: "momentum", 2: "condition", 3: "prescale", 4: "norm",
                 5: "gram", 6: "poly", 7: "combine", 8: "postnorm", 9: "update", 10: "thin_energy",
@@ -98,6 +98,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.muon_plan_set_lr.restype = ctypes.c_int
     lib.muon_plan_reset.argtypes = [ctypes.c_void_p]
     lib.muon_plan_reset.restype = ctypes.c_int
+    lib.muon_plan_set_graph.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+    lib.muon_plan_set_graph.restype = ctypes.c_int
     lib.muon_plan_destroy.argtypes = [ctypes.c_void_p]
     lib.muon_plan_destroy.restype = None
     lib.muon_status_string.argtypes = [ctypes.c_int]
@@ -362,6 +364,10 @@ class Plan:
     def reset(self):
         """Call after writing to the momentum buffers outside the plan."""
         _check(self._lib.muon_plan_reset(self._handle))
+
+    def set_graph(self, enable: bool = True):
+        """Replay the launch sequence as a HIP graph (muon_plan_set_graph)."""
+        _check(self._lib.muon_plan_set_graph(self._handle, 1 if enable else 0))
 
     def close(self):
         if self._handle:

@@ -793,6 +793,20 @@ struct muon_plan {
   muon::Staging staging;
   int parity = 0;          // energy cache holding the energies of the current momentum
   bool cached = false;     // whether that cache is valid
+  // Graph replay (muon_plan_set_graph): one instantiated graph per state of
+  // the launch sequence (the energy-cache parity for Dimuon), captured on a
+  // private stream of the plan.
+  bool graph_on = false;
+  hipStream_t capture = nullptr;
+  hipGraphExec_t exec[2] = {nullptr, nullptr};
+
+  void drop_graphs() {
+    for (auto& e : exec)
+      if (e) {
+        (void)hipGraphExecDestroy(e);
+        e = nullptr;
+      }
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -887,9 +901,38 @@ muon_status_t muon_plan_step(muon_plan_t* plan, void* stream) {
   using namespace muon;
   g_last_error.clear();
   if (!plan) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
-  const muon_status_t st = launch_all(plan->p, make_args(plan->p, plan->cfg, plan->ws, plan->dimuon), plan->cf,
-                                      plan->cfg.ns_steps, plan->dimuon, plan->parity, plan->cached,
-                                      static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const StepArgs args = make_args(plan->p, plan->cfg, plan->ws, plan->dimuon);
+  muon_status_t st = MUON_OK;
+  // Graph replay for steps whose sequence is fixed: every Muon step, and
+  // Dimuon steps with cached energies (the first step after creation or a
+  // reset also computes them, and runs eagerly).  Steps timed through the
+  // launch-event hook run eagerly too.
+  const bool replay = plan->graph_on && (!plan->dimuon || plan->cached) && !g_hook.events;
+  if (replay) {
+    hipGraphExec_t& exec = plan->exec[plan->dimuon ? plan->parity : 0];
+    if (!exec) {
+      hipGraph_t graph = nullptr;
+      MUON_HIP_TRY(hipStreamBeginCapture(plan->capture, hipStreamCaptureModeThreadLocal));
+      st = launch_all(plan->p, args, plan->cf, plan->cfg.ns_steps, plan->dimuon, plan->parity, plan->cached,
+                      plan->capture);
+      const hipError_t e = hipStreamEndCapture(plan->capture, &graph);
+      if (st != MUON_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return st;
+      }
+      if (e != hipSuccess) return fail(MUON_ERR_HIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
+      const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(graph);
+      if (ei != hipSuccess) {
+        exec = nullptr;
+        return fail(MUON_ERR_HIP, "hipGraphInstantiate: %s", hipGetErrorString(ei));
+      }
+    }
+    MUON_HIP_TRY(hipGraphLaunch(exec, s));
+  } else {
+    st = launch_all(plan->p, args, plan->cf, plan->cfg.ns_steps, plan->dimuon, plan->parity, plan->cached, s);
+  }
   if (st == MUON_OK && plan->dimuon) {
     // Pass A wrote the energies of the new momentum into the other cache.
     plan->parity ^= 1;
@@ -909,13 +952,31 @@ muon_status_t muon_plan_set_lr(muon_plan_t* plan, float lr) {
   using namespace muon;
   if (!plan) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
   if (!finite(lr)) return fail(MUON_ERR_INVALID_ARG, "lr must be finite");
+  if (lr != plan->cfg.lr) plan->drop_graphs();   // the rate is a kernel argument of the captured launches
   plan->cfg.lr = lr;
+  return MUON_OK;
+}
+
+muon_status_t muon_plan_set_graph(muon_plan_t* plan, int32_t enable) {
+  using namespace muon;
+  g_last_error.clear();
+  if (!plan) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
+  if (enable && !plan->capture) {
+    const hipError_t e = hipStreamCreateWithFlags(&plan->capture, hipStreamNonBlocking);
+    if (e != hipSuccess) {
+      plan->capture = nullptr;
+      return fail(MUON_ERR_HIP, "hipStreamCreateWithFlags: %s", hipGetErrorString(e));
+    }
+  }
+  plan->graph_on = enable != 0;
   return MUON_OK;
 }
 
 void muon_plan_destroy(muon_plan_t* plan) {
   if (!plan) return;
   plan->staging.release();
+  plan->drop_graphs();
+  if (plan->capture) (void)hipStreamDestroy(plan->capture);
   delete plan;
 }
 

@@ -226,6 +226,17 @@ muon_status_t muon_plan_step(muon_plan_t* plan, void* stream);
 muon_status_t muon_plan_reset(muon_plan_t* plan);
 /* Learning rate used by later steps of the plan (must be finite). */
 muon_status_t muon_plan_set_lr(muon_plan_t* plan, float lr);
+/* Replay the plan's launch sequence as a HIP graph (enable != 0) or launch
+ * its kernels one by one (enable = 0, the default).  With graphs on, the
+ * first step in each state of the sequence captures it (on a private stream
+ * the plan creates; a Dimuon plan alternates between two states) and every
+ * step then launches the instantiated graph on `stream`.  Results are the
+ * same bit for bit.  Steps that run eagerly even with graphs on: a Dimuon
+ * plan's first step and the step after muon_plan_reset (they also compute
+ * the energies of M_{t-1}), and steps timed through muon_set_launch_events.
+ * muon_plan_set_lr with a new rate discards the captured graphs.
+ * Errors: INVALID_ARG (NULL plan), HIP. */
+muon_status_t muon_plan_set_graph(muon_plan_t* plan, int32_t enable);
 /* Waits for the plan's upload to finish, then frees the plan (NULL is a no-op). */
 void muon_plan_destroy(muon_plan_t* plan);
 

@@ -414,6 +414,41 @@ def test_plan_matches_stateless_step_bitwise():
     plan.close()
 
 
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
+def test_plan_graph_replays_match_eager(variant):
+    # A plan replaying its launch sequence as a HIP graph equals a plan
+    # launching eagerly, bit for bit, step after step: graphs captured in
+    # both energy-cache states (Dimuon), eager device work and host
+    # synchronisations between the replays, and a learning-rate change
+    # (which discards the graphs).
+    shapes = [(8, 4096), (4096, 8), (300, 700), (700, 300), (16, 2048)]
+    wl = W.random_batch(shapes, dtype="bf16", ns_dtype="bf16", seed=23, variant=variant)
+    cfg = cfg_of(wl)
+    def fresh():
+        return [D.Param(w=m.w.cuda().clone(), g=m.g.cuda().clone(), mom=m.m_prev.cuda().clone(),
+                        o_out=torch.empty(m.shape, device="cuda")) for m in wl.mats]
+    a, b = fresh(), fresh()
+    pa, pb = D.Plan(a, cfg, dimuon=(variant == "dimuon")), D.Plan(b, cfg, dimuon=(variant == "dimuon"))
+    pb.set_graph(True)
+    junk = torch.ones(1 << 20, device="cuda")
+    for step in range(6):
+        if step == 4:
+            pa.set_lr(0.01)
+            pb.set_lr(0.01)
+        announce(f"graph replay {variant} step {step}")
+        pa.step()
+        pb.step()
+        junk.mul_(1.0001)          # the program's own eager work between replays
+        torch.cuda.synchronize()
+        for i, (x, y) in enumerate(zip(a, b)):
+            for name in ("w", "mom", "o_out"):
+                np.testing.assert_array_equal(getattr(x, name).float().cpu().numpy(),
+                                              getattr(y, name).float().cpu().numpy(),
+                                              err_msg=f"step {step} matrix {i} {name}")
+    pa.close()
+    pb.close()
+
+
 @pytest.mark.parametrize("shapes", [[(8, 4096), (4096, 8), (3, 1000), (16, 2048)], [(300, 700), (8, 300)]])
 def test_plan_steps_with_cached_energies_match_stateless(shapes):
     # A Dimuon plan reuses the energies its previous step computed; three plan
