@@ -346,6 +346,75 @@ def test_other_iteration_counts(steps):
     run_case(wl, "muon", cfg_of(wl, ns_steps=steps))
 
 
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
+def test_degenerate_shapes(variant):
+    # One-element and one-row matrices (thin path, Gram side 1) and the
+    # smallest general-path Gram side (33), f32 and bf16 storage.
+    shapes = [(1, 1), (1, 2), (2, 1), (1, 7), (33, 33), (33, 40), (40, 33)]
+    for dt in ("f32", "bf16"):
+        wl = W.random_batch(shapes, dtype=dt, ns_dtype="bf16", seed=29, variant=variant)
+        run_case(wl, variant, cfg_of(wl))
+
+
+def _batch_params(wl, idx):
+    return [D.Param(w=wl.mats[i].w.cuda().clone(), g=wl.mats[i].g.cuda().clone(),
+                    mom=wl.mats[i].m_prev.cuda().clone(),
+                    o_out=torch.full(wl.mats[i].shape, float("nan"), device="cuda")) for i in idx]
+
+
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
+def test_matrices_independent_of_batch(variant):
+    # A matrix's step does not depend on the other matrices of its batch:
+    # each matrix stepped alone equals the same matrix in a mixed batch, bit
+    # for bit (the batch changes tile lists and their order, not the
+    # arithmetic of any matrix).
+    shapes = [(8, 4096), (300, 700), (4096, 8), (700, 300), (256, 1024), (5, 333)]
+    wl = W.random_batch(shapes, dtype="bf16", ns_dtype="bf16", seed=31, variant=variant)
+    cfg = cfg_of(wl)
+    fn = D.dimuon_step if variant == "dimuon" else D.muon_step
+    announce(f"batch independence {variant}")
+    together = _batch_params(wl, range(wl.count))
+    fn(together, cfg)
+    for i in range(wl.count):
+        alone = _batch_params(wl, [i])
+        fn(alone, cfg)
+        torch.cuda.synchronize()
+        for name in ("w", "mom", "o_out"):
+            np.testing.assert_array_equal(getattr(alone[0], name).float().cpu().numpy(),
+                                          getattr(together[i], name).float().cpu().numpy(),
+                                          err_msg=f"matrix {i} {name}")
+
+
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
+def test_nonfinite_gradient_stays_in_its_matrix(variant):
+    # NaN propagates as IEEE arithmetic does (no status word): a NaN in one
+    # element of a gradient gives a NaN in that element of M_t and a
+    # non-finite step for that matrix (its norm is NaN), and leaves every
+    # other matrix of the batch bit-identical to a batch without it.
+    shapes = [(8, 1024), (300, 700), (1024, 8), (256, 256)]
+    wl = W.random_batch(shapes, dtype="bf16", ns_dtype="bf16", seed=37, variant=variant)
+    cfg = cfg_of(wl)
+    fn = D.dimuon_step if variant == "dimuon" else D.muon_step
+    for bad in (0, 1):
+        announce(f"NaN in gradient of matrix {bad} ({variant})")
+        clean = _batch_params(wl, range(wl.count))
+        dirty = _batch_params(wl, range(wl.count))
+        dirty[bad].g[3, 5] = float("nan")
+        fn(clean, cfg)
+        fn(dirty, cfg)
+        torch.cuda.synchronize()
+        m = dirty[bad].mom.float().cpu().numpy()
+        assert np.isnan(m[3, 5]) and np.isfinite(np.delete(m.ravel(), 3 * m.shape[1] + 5)).all()
+        assert not np.isfinite(dirty[bad].o_out.cpu().numpy()).any()
+        for i in range(wl.count):
+            if i == bad:
+                continue
+            for name in ("w", "mom", "o_out"):
+                np.testing.assert_array_equal(getattr(clean[i], name).float().cpu().numpy(),
+                                              getattr(dirty[i], name).float().cpu().numpy(),
+                                              err_msg=f"matrix {i} {name}")
+
+
 def test_zero_gradient_and_momentum_gives_zero_step():
     wl = W.random_batch([(8, 256), (130, 260)], dtype="bf16", ns_dtype="bf16", seed=11, zero_prev=True,
                         grad_std=0.0)
