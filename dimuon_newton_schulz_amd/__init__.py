@@ -35,7 +35,7 @@ EXPORTED_SYMBOLS = ("muon_config_default", "muon_workspace_bytes", "muon_step", 
 
 LAUNCH_KINDS = {-1: "start", 0: "thin_b", 1: "momentum", 2: "condition", 3: "prescale", 4: "norm",
                 5: "gram", 6: "poly", 7: "combine", 8: "postnorm", 9: "update", 10: "thin_energy",
-                11: "thin_a", 12: "momentum_prescale"}
+                11: "thin_a", 12: "momentum_prescale", 13: "energy"}
 
 
 class MuonMatrix(ctypes.Structure):

@@ -67,7 +67,7 @@ bool finite(float x) { return std::isfinite(x); }
 // ---------------------------------------------------------------------------
 struct Plan {
   std::vector<MatDesc> desc;
-  std::vector<Tile> k1, k3, k5, cond;
+  std::vector<Tile> k3, k5, cond;
   // GEMM tile lists, one launch each; bm x bn tiles (symmetric products: square)
   struct GemmList { int bm, bn; std::vector<Tile> tiles; size_t off; };
   std::vector<GemmList> syrk, comb;
@@ -83,7 +83,7 @@ struct Plan {
   struct ThinGroup { int kp; std::vector<Tile> tiles; size_t off; };
   std::vector<ThinGroup> thin;
   // byte offsets in the workspace
-  size_t desc_off = 0, scal_off = 0, k1_off = 0, k3_off = 0, k5_off = 0, cond_off = 0, gen_off = 0;
+  size_t desc_off = 0, scal_off = 0, k3_off = 0, k5_off = 0, cond_off = 0, gen_off = 0;
   size_t table_bytes = 0;   // uploaded prefix of the workspace
   size_t total_bytes = 0;   // whole workspace
   std::vector<unsigned char> table;
@@ -366,7 +366,6 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
     d.tall = x.m > x.n ? 1 : 0;
     d.update_scale = x.update_scale;
     d.scal_idx = static_cast<int32_t>(i);
-    d.v_off = -1;
     if (is_thin(x.m, x.n)) {
       d.KP = next_pow2(d.k);
       d.NP = d.N;
@@ -379,12 +378,10 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
       d.NP = static_cast<int32_t>(round_up(d.N, kPad));
       d.mpad = d.tall ? d.NP : d.KP;
       d.npad = d.tall ? d.KP : d.NP;
-      d.ncb = static_cast<int32_t>(ceil_div(d.n, 512));
-      d.nrb = static_cast<int32_t>(ceil_div(d.m, 32));
+      d.ncb = static_cast<int32_t>(ceil_div(d.n, 64));
+      d.nrb = static_cast<int32_t>(ceil_div(d.m, 64));
       d.n_pn = (d.KP / 64) * (d.NP / 64);
       p.gen.push_back(static_cast<uint16_t>(i));
-      for (int rb = 0; rb < d.nrb; ++rb)
-        for (int cb = 0; cb < d.ncb; ++cb) p.k1.push_back({static_cast<uint16_t>(i), (uint16_t)rb, (uint16_t)cb, 0});
       for (int ti = 0; ti < d.KP / 64; ++ti)
         for (int tj = 0; tj < d.NP / 64; ++tj) p.k3.push_back({static_cast<uint16_t>(i), (uint16_t)ti, (uint16_t)tj, 0});
       for (int ti = 0; ti < ceil_div(d.m, 64); ++ti)
@@ -406,7 +403,6 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
   };
   p.desc_off = take(sizeof(MatDesc) * count);
   p.scal_off = take(sizeof(MatScal) * count);
-  p.k1_off = take(sizeof(Tile) * p.k1.size());
   p.k3_off = take(sizeof(Tile) * p.k3.size());
   for (auto& l : p.syrk) l.off = take(sizeof(Tile) * l.tiles.size());
   for (auto& l : p.comb) l.off = take(sizeof(Tile) * l.tiles.size());
@@ -440,12 +436,11 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
     d.a_off = take(static_cast<size_t>(d.KP) * d.KP * es);
     d.b_off = take(static_cast<size_t>(p.rows[i]) * d.KP * es);
     d.z_off = take(kn * es);
-    if (cfg->nesterov) d.v_off = take(static_cast<size_t>(d.m) * d.n * 4);
     d.dr_off = take(static_cast<size_t>(d.mpad) * 4);
     d.dc_off = take(static_cast<size_t>(d.npad) * 4);
     d.cm_off = take(static_cast<size_t>(d.ncond) * 8);
-    d.pr_off = take(static_cast<size_t>(d.ncb) * d.m * 4);
-    d.pc_off = take(static_cast<size_t>(d.nrb) * d.n * 4);
+    for (int par = 0; par < 2; ++par)
+      d.ge_off[par] = take((static_cast<size_t>(d.ncb) * d.m + static_cast<size_t>(d.nrb) * d.n) * 4);
     d.pn_off = take(static_cast<size_t>(d.n_pn) * 4);
     d.pz_off = take(static_cast<size_t>(d.n_pz) * 8);
   }
@@ -454,7 +449,6 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
   if (with_table) {
     p.table.assign(p.table_bytes, 0);
     std::memcpy(p.table.data() + p.desc_off, p.desc.data(), sizeof(MatDesc) * count);
-    put(p.table, p.k1_off, p.k1);
     put(p.table, p.k3_off, p.k3);
     for (auto& l : p.syrk) put(p.table, l.off, l.tiles);
     for (auto& l : p.comb) put(p.table, l.off, l.tiles);
@@ -631,8 +625,9 @@ void make_coeffs(const muon_config_t& cfg, Coeffs* cf) {
 
 // The launch sequence of one step; the descriptor table is already on the
 // device (ordered before these launches on stream s).
-// `parity` selects the thin path's energy cache holding the energies of
-// M_{t-1}; `cached` says whether it is valid (else it is computed first).
+// `parity` selects the energy caches (thin and general path) holding the
+// energies of M_{t-1}; `cached` says whether they are valid (else they are
+// computed first).  The step writes the energies of M_t into the others.
 muon_status_t launch_all(const Plan& p, const StepArgs& a, const Coeffs* cf, int ns_steps, bool dimuon,
                          int parity, bool cached, hipStream_t s) {
   char* base = a.ws;
@@ -652,16 +647,17 @@ muon_status_t launch_all(const Plan& p, const StepArgs& a, const Coeffs* cf, int
     const int n3 = static_cast<int>(p.k3.size());
     if (dimuon) {
       // The factors need the energies of M_{t-1} (a reduction over whole rows
-      // and columns) before anything is scaled: momentum with the energy
-      // partials, the factors, then the prescale of M_t.
+      // and columns) before anything is scaled.  The previous step of a plan
+      // left them in cache `parity`; otherwise a pass over M_{t-1} puts them
+      // there first.
       const int nc = static_cast<int>(p.cond.size());
-      MUON_LAUNCH(MUON_LAUNCH_MOMENTUM, launch_momentum(a, tl(p.k1_off), static_cast<int>(p.k1.size()), true, s));
-      MUON_LAUNCH(MUON_LAUNCH_CONDITION, launch_cond_energy(a, tl(p.cond_off), nc, s));
+      if (!cached) MUON_LAUNCH(MUON_LAUNCH_ENERGY, launch_energy(a, tl(p.k3_off), n3, parity, s));
+      MUON_LAUNCH(MUON_LAUNCH_CONDITION, launch_cond_energy(a, tl(p.cond_off), nc, parity, s));
       MUON_LAUNCH(MUON_LAUNCH_CONDITION, launch_cond_factor(a, tl(p.cond_off), nc, s));
-      MUON_LAUNCH(MUON_LAUNCH_PRESCALE, launch_prescale(a, tl(p.k3_off), n3, false, s));
-    } else {
-      MUON_LAUNCH(MUON_LAUNCH_MOMENTUM_PRESCALE, launch_prescale(a, tl(p.k3_off), n3, true, s));
     }
+    // Momentum, the energies of M_t (Dimuon, into the other cache) and the
+    // prescale in one pass.
+    MUON_LAUNCH(MUON_LAUNCH_MOMENTUM_PRESCALE, launch_prescale(a, tl(p.k3_off), n3, dimuon, parity ^ 1, s));
     MUON_LAUNCH(MUON_LAUNCH_NORM, launch_norm_finalize(a, il(p.gen_off), ng, s));
     auto nt = [](const Plan::GemmList& l) { return static_cast<int>(l.tiles.size()); };
     if (ns_steps == 0)

@@ -42,17 +42,16 @@ struct alignas(16) MatDesc {
   int64_t a_off;          // A = X X^T, KP x KP, ns dtype
   int64_t b_off;          // B = bA + c A A, KP x KP, ns dtype
   int64_t z_off;          // Z (last iterate), KP x NP (transposed for tall), ns dtype
-  int64_t v_off;          // Nesterov input, m x n f32 (or -1)
   int64_t dr_off;         // row factors, mpad f32 (zero beyond m)
   int64_t dc_off;         // column factors, npad f32 (zero beyond n)
   int64_t cm_off;         // conditioning chunk maxima [ncond][2] f32 (rows, columns)
   int32_t ncond;          // conditioning chunks of 256 over the padded rows, then columns
   int32_t mpad, npad;     // padded m and n: KP and NP in the caller's orientation
-  int64_t pr_off;         // row-energy partials [ncb][m] f32
-  int64_t pc_off;         // column-energy partials [nrb][n] f32
+  int64_t ge_off[2];      // energy cache, two parities: row partials [ncb][m] over 64-column blocks,
+                          // then column partials [nrb][n] over 64-row blocks, f32
   int64_t pn_off;         // ||Y||^2 partials, one per prescale tile, f32
   int64_t pz_off;         // (||Z||^2, ||P||^2) partials, one pair per 128 x 128 sub-tile of the combine, f32
-  int32_t ncb, nrb;       // number of 512-column / 32-row energy blocks
+  int32_t ncb, nrb;       // number of 64-column / 64-row energy blocks
   int32_t n_pn, n_pz;     // partial counts
   int32_t scal_idx;       // index into the per-matrix scalar array
   // Thin path (Gram side <= 32): the long side is cut into S slices of L positions.
@@ -324,13 +323,16 @@ __device__ __forceinline__ float cond_factor(float e, float emax, float eps) {
 // --------------------------------------------------------------------------
 // Host-side launchers (defined in the .hip files)
 // --------------------------------------------------------------------------
-hipError_t launch_momentum(const StepArgs& a, const Tile* tiles, int n, bool energies, hipStream_t s);
+// Energy partials of M_{t-1} into cache `parity` (tiles: the prescale's).
+hipError_t launch_energy(const StepArgs& a, const Tile* tiles, int n, int parity, hipStream_t s);
 // Dimuon conditioning over chunks of 256 rows / columns (tiles: matrix,
-// chunk): energies and chunk maxima, then the factors (zero in the padding).
-hipError_t launch_cond_energy(const StepArgs& a, const Tile* tiles, int n, hipStream_t s);
+// chunk): energies (from cache `parity`) and chunk maxima, then the factors
+// (zero in the padding).
+hipError_t launch_cond_energy(const StepArgs& a, const Tile* tiles, int n, int parity, hipStream_t s);
 hipError_t launch_cond_factor(const StepArgs& a, const Tile* tiles, int n, hipStream_t s);
-// Prescale; `momentum` (Muon only): the momentum update in the same pass.
-hipError_t launch_prescale(const StepArgs& a, const Tile* tiles, int n, bool momentum, hipStream_t s);
+// Momentum, then (Dimuon, `energies`) the energy partials of M_t into cache
+// `out_parity`, and the prescale, in one pass.
+hipError_t launch_prescale(const StepArgs& a, const Tile* tiles, int n, bool energies, int out_parity, hipStream_t s);
 hipError_t launch_norm_finalize(const StepArgs& a, const uint16_t* mats, int n, hipStream_t s);
 hipError_t launch_post_finalize(const StepArgs& a, const uint16_t* mats, int n, hipStream_t s);
 hipError_t launch_update(const StepArgs& a, const Tile* tiles, int n, hipStream_t s);

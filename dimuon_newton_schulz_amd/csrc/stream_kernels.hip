@@ -1,8 +1,9 @@
-// HBM-streaming kernels of the general path: momentum (+ Dimuon energies),
-// conditioning, prescale into the Gram orientation, norm finalisation, and
-// the final update.  No FMA contraction in this file: the energies must
-// follow the stated float32 tree exactly, so every fused multiply-add below
-// is written out as __builtin_fmaf.
+// HBM-streaming kernels of the general path: the energies of M_{t-1} (only
+// when no cached ones exist), conditioning, the fused momentum / energies /
+// prescale pass into the Gram orientation, norm finalisation, and the final
+// update.  No FMA contraction in this file: the energies must follow the
+// stated float32 tree exactly, so every fused multiply-add below is written
+// out as __builtin_fmaf.
 #pragma clang fp contract(off)
 
 #include "common.h"
@@ -62,96 +63,83 @@ __device__ __forceinline__ void store8(void* p, int32_t dt, int64_t rowoff, int 
 }
 
 // ---------------------------------------------------------------------------
-// K1: M_t = mu * M_{t-1} + G, written in the momentum dtype; optionally the
-// Nesterov input G + mu * M_t (f32, workspace); optionally the float32
-// energy partials of M_{t-1}.
-//
-// Tile: 32 rows x 512 columns; wave w owns rows 8w .. 8w+7, lane l owns
-// columns 8l .. 8l+7.  Row partial over the tile's 512 columns: in-lane
-// pairwise over 8, then the wave butterfly -> pr[cb][row].  Column partial
-// over the tile's 32 rows: in-lane pairwise over the wave's 8 rows, then the
-// four waves pairwise -> pc[rb][col].  Both are aligned power-of-two blocks
-// of the stated tree.
+// Energy partials.  The general path cuts every matrix (in the caller's
+// orientation) into 64 x 64 blocks, the tiles of the prescale pass.  A
+// block contributes the row partial of each of its rows over its 64 columns
+// and the column partial of each of its columns over its 64 rows, both
+// aligned 64-element blocks of the stated pairwise tree (zero beyond the
+// matrix).  The cache of one parity holds the row partials [ncb][m], then
+// the column partials [nrb][n].
+// A thread holds row si0 + r, columns sj0 + c0 .. c0 + 15 (c0 = 16 (tid & 3),
+// r = tid / 4) of the block: its 16 squares are summed pairwise in the
+// thread, then the four threads of the row (lanes 4q .. 4q+3 of a wave) are
+// added pairwise.  The columns go through LDS: thread t sums column t mod 64
+// over rows 16 (t / 64) .. + 15 pairwise, and the four 16-row sums of a
+// column are added pairwise.
 // ---------------------------------------------------------------------------
-// Eight waves per SIMD (64 VGPRs; the default allocation took 66 and seven
-// waves): the row-at-a-time loop keeps one row of M and G in flight per
-// wave, so waves are what keep the memory system busy.
-__global__ __launch_bounds__(256, 8) void k_momentum(StepArgs a, const Tile* __restrict__ tiles,
-                                                  int energies) {
-  __shared__ float red[4][512];
+template <int CNT>
+__device__ __forceinline__ float tree_sum(const float* x) {
+  if constexpr (CNT == 1) return x[0];
+  else return tree_sum<CNT / 2>(x) + tree_sum<CNT / 2>(x + CNT / 2);
+}
+
+__device__ __forceinline__ void block_energies(const float (&p)[16], int si0, int sj0, const MatDesc& d,
+                                               float* cache, float (*pS)[65], float (*part)[64]) {
+  const int tid = threadIdx.x, r = tid >> 2, c0 = (tid & 3) * 16;
+  const int m = d.m, n = d.n;
+  float rs = tree_sum<16>(p);
+  rs = rs + dpp_f32<0xB1>(rs);   // quad_perm [1,0,3,2]: (q0 + q1), (q2 + q3)
+  rs = rs + dpp_f32<0x4E>(rs);   // quad_perm [2,3,0,1]: (q0 + q1) + (q2 + q3)
+  if ((tid & 3) == 0 && si0 + r < m && sj0 < n) cache[static_cast<int64_t>(sj0 / 64) * m + si0 + r] = rs;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) pS[r][c0 + e] = p[e];
+  __syncthreads();
+  {
+    const int c = tid & 63, q = tid >> 6;
+    float col[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) col[i] = pS[16 * q + i][c];
+    part[q][c] = tree_sum<16>(col);
+  }
+  __syncthreads();
+  if (tid < 64 && si0 < m && sj0 + tid < n) {
+    float* pc = cache + static_cast<int64_t>(d.ncb) * m;
+    pc[static_cast<int64_t>(si0 / 64) * n + sj0 + tid] = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
+  }
+}
+
+// Source block of a prescale tile: Gram element (ga, gb) is source (ga, gb)
+// when wide, (gb, ga) when tall.
+__device__ __forceinline__ void source_block(const MatDesc& d, const Tile& t, int& si0, int& sj0) {
+  const int ga0 = t.ti * 64, gb0 = t.tj * 64;
+  si0 = d.tall ? gb0 : ga0;
+  sj0 = d.tall ? ga0 : gb0;
+}
+
+// Energies of M_{t-1} into cache `parity` (no cached energies: stateless
+// calls, a plan's first Dimuon step, or after a reset).  Tiles: the
+// prescale's (one 64 x 64 block each).
+__global__ __launch_bounds__(256) void k_energy(StepArgs a, const Tile* __restrict__ tiles, int parity) {
+  __shared__ float pS[64][65];
+  __shared__ float part[4][64];
   const Tile t = tiles[blockIdx.x];
   const MatDesc& d = a.desc[t.mat];
-  const int m = d.m, n = d.n;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col0 = t.tj * 512 + lane * 8;
-  const int row_base = t.ti * 32 + wave * 8;
-  float* vbuf = (a.nesterov && d.v_off >= 0) ? reinterpret_cast<float*>(a.ws + d.v_off) : nullptr;
-
-  // Binary-counter pairwise over the wave's 8 rows, per column.
-  float lvl0[8], lvl1[8], lvl2[8];
+  int si0, sj0;
+  source_block(d, t, si0, sj0);
+  const int tid = threadIdx.x, r = tid >> 2, c0 = (tid & 3) * 16;
+  const int row = si0 + r;
+  float v[16];
+  if (row < d.m) {
+    const int64_t off = static_cast<int64_t>(row) * d.n;
+    load8(d.mom, a.mom_dt, off, sj0 + c0, d.n, v);
+    load8(d.mom, a.mom_dt, off, sj0 + c0 + 8, d.n, v + 8);
+  } else {
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int row = row_base + r;
-    float mp[8], g[8], mn[8];
-    const bool in = row < m;
-    const int64_t off = static_cast<int64_t>(row) * n;
-    if (in) {
-      load8(d.mom, a.mom_dt, off, col0, n, mp);
-      load8(d.g, a.g_dt, off, col0, n, g);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { mp[e] = 0.0f; g[e] = 0.0f; }
-    }
-    if (energies) {
-      float p[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = mp[e] * mp[e];
-      // row partial: in-lane pairwise over 8, then the butterfly over 64 lanes
-      float s = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      s = wave_tree_sum(s);
-      if (in && lane == 0)
-        reinterpret_cast<float*>(a.ws + d.pr_off)[static_cast<int64_t>(t.tj) * m + row] = s;
-      // column partial: binary counter over r
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if ((r & 1) == 0) {
-          lvl0[e] = p[e];
-        } else {
-          float c1 = lvl0[e] + p[e];
-          if ((r & 2) == 0) {
-            lvl1[e] = c1;
-          } else {
-            float c2 = lvl1[e] + c1;
-            if ((r & 4) == 0) lvl2[e] = c2;
-            else lvl2[e] = lvl2[e] + c2;
-          }
-        }
-      }
-    }
-    if (in) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mn[e] = momentum_value(a.mu, mp[e], g[e], a.mom_dt);
-      store8(d.mom, a.mom_dt, off, col0, n, mn);
-      if (vbuf) {
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = g[e] + a.mu * mn[e];
-        store8(vbuf, DT_F32, off, col0, n, v);
-      }
-    }
+    for (int e = 0; e < 16; ++e) v[e] = 0.0f;
   }
-  if (!energies) return;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) red[wave][lane * 8 + e] = lvl2[e];
-  __syncthreads();
-  float* pc = reinterpret_cast<float*>(a.ws + d.pc_off);
-  for (int c = threadIdx.x; c < 512; c += 256) {
-    const int col = t.tj * 512 + c;
-    if (col < n) {
-      float s = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
-      pc[static_cast<int64_t>(t.ti) * n + col] = s;
-    }
-  }
+  for (int e = 0; e < 16; ++e) v[e] = v[e] * v[e];
+  block_energies(v, si0, sj0, d, reinterpret_cast<float*>(a.ws + d.ge_off[parity]), pS, part);
 }
 
 // ---------------------------------------------------------------------------
@@ -173,7 +161,7 @@ __device__ float block_max(float v, float* sh) {
 }
 
 
-__global__ __launch_bounds__(256) void k_cond_energy(StepArgs a, const Tile* __restrict__ tiles) {
+__global__ __launch_bounds__(256) void k_cond_energy(StepArgs a, const Tile* __restrict__ tiles, int parity) {
   __shared__ float sh[8];
   const Tile t = tiles[blockIdx.x];
   const MatDesc& d = a.desc[t.mat];
@@ -182,8 +170,8 @@ __global__ __launch_bounds__(256) void k_cond_energy(StepArgs a, const Tile* __r
   const int idx = t.ti * 256 + threadIdx.x;
   MUON_GLOBAL float* dr = gmem(reinterpret_cast<float*>(a.ws + d.dr_off));
   MUON_GLOBAL float* dc = gmem(reinterpret_cast<float*>(a.ws + d.dc_off));
-  const float* pr = reinterpret_cast<const float*>(a.ws + d.pr_off);
-  const float* pc = reinterpret_cast<const float*>(a.ws + d.pc_off);
+  const float* pr = reinterpret_cast<const float*>(a.ws + d.ge_off[parity]);
+  const float* pc = pr + static_cast<int64_t>(d.ncb) * m;
   float rmax = 0.0f, cmax = 0.0f;
   if (idx < mp) {
     const int i = idx;
@@ -248,17 +236,21 @@ __global__ __launch_bounds__(256) void k_cond_factor(StepArgs a, const Tile* __r
 }
 
 // ---------------------------------------------------------------------------
-// K3: Y = D_R * V * D_C (V = M_t, or the Nesterov input), rounded to the NS
-// dtype, written in the Gram orientation (KP x NP) and its transpose
-// (NP x KP), zero in the padding; one ||Y||^2 partial per tile.
-// Tile: 64 x 64 of the Gram orientation; the source tile goes through LDS.
-// MOM (Muon, which needs no energies): the momentum update happens here as
-// well, M_t = mu M_{t-1} + G computed from the loaded M_{t-1} and G and
-// stored, so M_t is not read back; each element belongs to one tile.
+// K3: the fused pass.  M_t = mu M_{t-1} + G (correctly rounded to the
+// momentum dtype and stored); with ENERGIES (Dimuon) the energy partials of
+// M_t into cache `out_parity`, for the next step's conditioning; then
+// Y = D_R V D_C (V = M_t, or the Nesterov input G + mu M_t), rounded to the
+// NS dtype, written in the Gram orientation (KP x NP) and, for the fp32
+// products, its transpose (NP x KP), zero in the padding; one ||Y||^2
+// partial per tile.  Tile: 64 x 64 of the Gram orientation; the source
+// block goes through LDS.  Each element belongs to one tile, so M_t is
+// never read back.
 // ---------------------------------------------------------------------------
-template <bool MOM>
-__global__ __launch_bounds__(256) void k_prescale(StepArgs a, const Tile* __restrict__ tiles) {
+template <bool ENERGIES>
+__global__ __launch_bounds__(256) void k_prescale(StepArgs a, const Tile* __restrict__ tiles, int out_parity) {
   __shared__ float tileS[64][65];
+  __shared__ float pS[ENERGIES ? 64 : 1][65];
+  __shared__ float part[ENERGIES ? 4 : 1][64];
   __shared__ float red[4];
   const Tile t = tiles[blockIdx.x];
   const MatDesc& d = a.desc[t.mat];
@@ -267,35 +259,31 @@ __global__ __launch_bounds__(256) void k_prescale(StepArgs a, const Tile* __rest
   const bool cond = a.dimuon && a.scal[d.scal_idx].cond_on != 0.0f;
   const float* dr = reinterpret_cast<const float*>(a.ws + d.dr_off);
   const float* dc = reinterpret_cast<const float*>(a.ws + d.dc_off);
-  const bool use_v = !MOM && a.nesterov && d.v_off >= 0;
-  const void* src = use_v ? static_cast<const void*>(a.ws + d.v_off) : static_cast<const void*>(d.mom);
-  const int sdt = use_v ? DT_F32 : a.mom_dt;
-
-  // Source tile in the original orientation: rows si0.., cols sj0..
-  // Gram element (ga, gb) <- source (ga, gb) when wide, (gb, ga) when tall.
   const int ga0 = t.ti * 64, gb0 = t.tj * 64;
-  const int si0 = d.tall ? gb0 : ga0;
-  const int sj0 = d.tall ? ga0 : gb0;
+  int si0, sj0;
+  source_block(d, t, si0, sj0);
   {
     const int r = tid >> 2, c0 = (tid & 3) * 16;
     const int row = si0 + r;
-    float v[16];
+    float v[16], sq[16];
     if (row < m) {
       const int64_t off = static_cast<int64_t>(row) * n;
-      load8(src, sdt, off, sj0 + c0, n, v);
-      load8(src, sdt, off, sj0 + c0 + 8, n, v + 8);
-      if constexpr (MOM) {
-        float gv[16];
-        load8(d.g, a.g_dt, off, sj0 + c0, n, gv);
-        load8(d.g, a.g_dt, off, sj0 + c0 + 8, n, gv + 8);
+      float gv[16];
+      load8(d.mom, a.mom_dt, off, sj0 + c0, n, v);
+      load8(d.mom, a.mom_dt, off, sj0 + c0 + 8, n, v + 8);
+      load8(d.g, a.g_dt, off, sj0 + c0, n, gv);
+      load8(d.g, a.g_dt, off, sj0 + c0 + 8, n, gv + 8);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) v[e] = momentum_value(a.mu, v[e], gv[e], a.mom_dt);
-        store8(d.mom, a.mom_dt, off, sj0 + c0, n, v);
-        store8(d.mom, a.mom_dt, off, sj0 + c0 + 8, n, v + 8);
-        if (a.nesterov) {
+      for (int e = 0; e < 16; ++e) v[e] = momentum_value(a.mu, v[e], gv[e], a.mom_dt);
+      store8(d.mom, a.mom_dt, off, sj0 + c0, n, v);
+      store8(d.mom, a.mom_dt, off, sj0 + c0 + 8, n, v + 8);
+      if constexpr (ENERGIES) {
 #pragma unroll
-          for (int e = 0; e < 16; ++e) v[e] = gv[e] + a.mu * v[e];
-        }
+        for (int e = 0; e < 16; ++e) sq[e] = v[e] * v[e];   // fl32(x * x) of the stored value
+      }
+      if (a.nesterov) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = gv[e] + a.mu * v[e];
       }
       const float rf = cond ? dr[row] : 1.0f;
       // The thread's 16 column factors as four 16-byte loads (the factor
@@ -318,8 +306,13 @@ __global__ __launch_bounds__(256) void k_prescale(StepArgs a, const Tile* __rest
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) v[e] = 0.0f;
+      for (int e = 0; e < 16; ++e) {
+        v[e] = 0.0f;
+        sq[e] = 0.0f;
+      }
     }
+    if constexpr (ENERGIES)
+      block_energies(sq, si0, sj0, d, reinterpret_cast<float*>(a.ws + d.ge_off[out_parity]), pS, part);
 #pragma unroll
     for (int e = 0; e < 16; ++e) tileS[r][c0 + e] = round_to(v[e], a.ns_dt);
   }
@@ -515,15 +508,15 @@ __global__ __launch_bounds__(256) void k_update(StepArgs a, const Tile* __restri
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_momentum(const StepArgs& a, const Tile* tiles, int n, bool energies, hipStream_t s) {
+hipError_t launch_energy(const StepArgs& a, const Tile* tiles, int n, int parity, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_momentum, dim3(n), dim3(256), 0, s, a, tiles, energies ? 1 : 0);
+  hipLaunchKernelGGL(k_energy, dim3(n), dim3(256), 0, s, a, tiles, parity);
   return hipGetLastError();
 }
 
-hipError_t launch_cond_energy(const StepArgs& a, const Tile* tiles, int n, hipStream_t s) {
+hipError_t launch_cond_energy(const StepArgs& a, const Tile* tiles, int n, int parity, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_cond_energy, dim3(n), dim3(256), 0, s, a, tiles);
+  hipLaunchKernelGGL(k_cond_energy, dim3(n), dim3(256), 0, s, a, tiles, parity);
   return hipGetLastError();
 }
 
@@ -533,10 +526,10 @@ hipError_t launch_cond_factor(const StepArgs& a, const Tile* tiles, int n, hipSt
   return hipGetLastError();
 }
 
-hipError_t launch_prescale(const StepArgs& a, const Tile* tiles, int n, bool momentum, hipStream_t s) {
+hipError_t launch_prescale(const StepArgs& a, const Tile* tiles, int n, bool energies, int out_parity, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  if (momentum) hipLaunchKernelGGL(k_prescale<true>, dim3(n), dim3(256), 0, s, a, tiles);
-  else hipLaunchKernelGGL(k_prescale<false>, dim3(n), dim3(256), 0, s, a, tiles);
+  if (energies) hipLaunchKernelGGL(k_prescale<true>, dim3(n), dim3(256), 0, s, a, tiles, out_parity);
+  else hipLaunchKernelGGL(k_prescale<false>, dim3(n), dim3(256), 0, s, a, tiles, out_parity);
   return hipGetLastError();
 }
 

@@ -183,9 +183,9 @@ muon_status_t muon_step_noalloc(const muon_matrix_t* mats, int64_t count,
 typedef enum muon_launch_kind {
   MUON_LAUNCH_START = -1,     /* event recorded before the first launch */
   MUON_LAUNCH_THIN = 0,       /* thin path pass B: k x k iteration, next energies, apply, update */
-  MUON_LAUNCH_MOMENTUM = 1,   /* momentum (+ energy partials) */
+  MUON_LAUNCH_MOMENTUM = 1,   /* (not emitted: the momentum runs in the prescale pass) */
   MUON_LAUNCH_CONDITION = 2,  /* energies -> Dimuon factors */
-  MUON_LAUNCH_PRESCALE = 3,   /* conditioned, normalised bf16/f32 copy (+ transpose) */
+  MUON_LAUNCH_PRESCALE = 3,   /* (not emitted: see MOMENTUM_PRESCALE) */
   MUON_LAUNCH_NORM = 4,       /* Frobenius norm of the prescaled copy */
   MUON_LAUNCH_GRAM = 5,       /* A = X X^T */
   MUON_LAUNCH_POLY = 6,       /* B = b A + c A A */
@@ -194,7 +194,9 @@ typedef enum muon_launch_kind {
   MUON_LAUNCH_UPDATE = 9,     /* O and the weight update */
   MUON_LAUNCH_THIN_ENERGY = 10, /* thin path: energies of M_{t-1} (no cached energies) */
   MUON_LAUNCH_THIN_A = 11,    /* thin path pass A: momentum, Gram partials */
-  MUON_LAUNCH_MOMENTUM_PRESCALE = 12  /* Muon: momentum and prescale in one pass */
+  MUON_LAUNCH_MOMENTUM_PRESCALE = 12, /* momentum, Dimuon energies of M_t, conditioned and
+                                         normalised bf16/f32 copy (+ transpose), one pass */
+  MUON_LAUNCH_ENERGY = 13     /* energies of M_{t-1} (general path, no cached energies) */
 } muon_launch_kind_t;
 
 /* Timing hook, per host thread; not part of the method.  When `events` is
@@ -219,8 +221,8 @@ muon_status_t muon_plan_create(const muon_matrix_t* mats, int64_t count,
                                void* stream, muon_plan_t** plan);
 muon_status_t muon_plan_step(muon_plan_t* plan, void* stream);
 /* A Dimuon plan keeps, in its workspace, the row/column energies of the
- * momentum its last step wrote (the next step's R and C), so for matrices
- * with a Gram side <= 32 the next step need not read M_{t-1} twice.  Call
+ * momentum its last step wrote (the next step's R and C), so the next step
+ * need not read M_{t-1} an extra time to compute them.  Call
  * muon_plan_reset after writing to the momentum buffers outside the plan
  * (resume, reset); the next step then recomputes them.  Muon plans ignore it. */
 muon_status_t muon_plan_reset(muon_plan_t* plan);

@@ -138,10 +138,12 @@ def test_general_ragged_mixed_batch(variant, ns):
 
 @pytest.mark.parametrize("wdt", ["bf16", "f32"])
 def test_muon_streaming_passes_fused(wdt):
-    # Muon: the momentum update runs inside the prescale launch (M_t is not
-    # read back), so no separate momentum launch remains; Dimuon keeps it
-    # (its factors need the energies of M_{t-1} first).  Ragged and whole
-    # 16-byte runs, wide and tall, f32 and bf16 storage.
+    # The momentum update runs inside the prescale launch (M_t is not read
+    # back).  Dimuon's factors need the energies of M_{t-1} first: a
+    # stateless call computes them in a pass of their own, a plan step reads
+    # the ones its previous step left (the fused pass computes those of M_t),
+    # and a reset brings the extra pass back.  Ragged and whole 16-byte runs,
+    # wide and tall, f32 and bf16 storage.
     shapes = [(200, 333), (333, 200), (256, 1024), (1000, 130), (8, 512)]
     wl = W.random_batch(shapes, dtype=wdt, ns_dtype="bf16", seed=17)
     cfg = cfg_of(wl)
@@ -153,7 +155,14 @@ def test_muon_streaming_passes_fused(wdt):
     f32 = launch_kinds(lambda: D.muon_step(params, cfg_of(wl, ns_dtype="f32")))
     assert "momentum_prescale" in f32 and "momentum" not in f32, f32
     dim = launch_kinds(lambda: D.dimuon_step(params, cfg))
-    assert "momentum" in dim and "prescale" in dim and "momentum_prescale" not in dim, dim
+    assert dim.count("energy") == 1 and dim.count("momentum_prescale") == 1, dim
+    assert not {"momentum", "prescale"} & set(dim), dim
+    plan = D.Plan(params, cfg, dimuon=True)
+    first, second = launch_kinds(plan.step), launch_kinds(plan.step)
+    plan.reset()
+    third = launch_kinds(plan.step)
+    plan.close()
+    assert "energy" in first and "energy" not in second and "energy" in third, (first, second, third)
     del params
     run_case(wl, "muon", cfg)
     run_case(wl, "muon", cfg_of(wl, nesterov=True, weight_decay=0.1), scales=[0.5, 2.0, 1.0, 1.5, 0.25])
