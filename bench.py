@@ -37,9 +37,9 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 # profiles/k_thin_lora_batch_64x8x4096.md.
 THIN_SOURCES = ("dimuon_newton_schulz_amd/csrc/thin_kernel.hip", "dimuon_newton_schulz_amd/csrc/common.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "088ff41bf390c971246bc767ae0125ecdaf043fb9952171f936677fcaace23e1",
-    "k_thin_a": {"fetch_kib": 18128.6, "write_kib": 19013.4},
-    "k_thin_b": {"fetch_kib": 20387.4, "write_kib": 18496.0},
+    "sources_sha256": "30c10725495475707d8e4c4a3f60c6abed661f71f1647953cb3809472d662332",
+    "k_thin_a": {"fetch_kib": 18158.2, "write_kib": 19012.7},
+    "k_thin_b": {"fetch_kib": 20425.0, "write_kib": 18496.0},
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
