@@ -115,7 +115,8 @@ __device__ __forceinline__ int qswz(int row) { return 4 * (row & 3); }
 // global chunk that belongs in its slot.
 // same: Q is P (a diagonal tile of a symmetric product); only P's rows are
 // loaded, and the fragments of both operands come from them.
-template <int BM, int BN, bool QT>
+// Loads Q0 .. Q1-1 of the thread's LA + LB (all of them by default).
+template <int BM, int BN, bool QT, int Q0 = 0, int Q1 = GemmT<BM, BN>::LPS>
 __device__ __forceinline__ void issue_stage(const MUON_GLOBAL uint16_t* P, int64_t ldp, const MUON_GLOBAL uint16_t* Q,
                                             int64_t ldq, int st, uint16_t* buf, bool same = false) {
   using G = GemmT<BM, BN>;
@@ -123,7 +124,7 @@ __device__ __forceinline__ void issue_stage(const MUON_GLOBAL uint16_t* P, int64
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int k0 = st * LBK;
 #pragma unroll
-  for (int q = 0; q < G::LA + G::LB; ++q) {
+  for (int q = Q0; q < Q1; ++q) {
     const bool is_a = q < G::LA;
     if (!is_a && same) break;
     const int blk = (is_a ? q : q - G::LA) * G::NW + wave;
@@ -252,10 +253,15 @@ __device__ __forceinline__ void mma_bf16(const uint16_t* Pg, int64_t ldp, const 
   // MFMAs of stage kt's last step, then stage kt+1's other steps.  The loop
   // is entered and closed at a sync, with no load in flight, so the compiler
   // keeps track of which buffer the loads in flight write.
+  // Half of stage kt+2's loads go out before the first MFMAs of the half
+  // step and half after them, so that the SIMD's two waves do not both sit
+  // in a run of load issues while the matrix core idles (1.4% faster on the
+  // 4096^2 set than all loads first).
   auto half_step = [&](uint16_t* cur, uint16_t* nxt, int kt) {
-    if (kt + 2 < nk) issue_stage<BM, BN, QT>(P, ldp, Q, ldq, kt + 2, cur, same);
+    if (kt + 2 < nk) issue_stage<BM, BN, QT, 0, LPS / 2>(P, ldp, Q, ldq, kt + 2, cur, same);
     read_step(nxt, 0, fa[0], fb[0]);
     mfma_step(fa[(NQ - 1) & 1], fb[(NQ - 1) & 1]);
+    if (kt + 2 < nk) issue_stage<BM, BN, QT, LPS / 2, LPS>(P, ldp, Q, ldq, kt + 2, cur, same);
 #pragma unroll
     for (int q = 1; q < NQ; ++q) {
       read_step(nxt, q, fa[q & 1], fb[q & 1]);

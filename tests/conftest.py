@@ -28,3 +28,24 @@ def pytest_terminal_summary(terminalreporter, exitstatus, config):
         extra = f" div {r['div_dO']:.2e}" if "div_dO" in r else ""
         tr.write_line(f"{r['case']}: max|dO| {r['max_abs_dO']:.3e} relF {r['rel_F_dO']:.2e} "
                       f"||O||ratio-1 {r['norm_ratio_m1']:+.2e} max|O| {r['max_abs_O']:.3f}{extra}")
+
+    path = os.environ.get("MUON_PARITY_SUMMARY")
+    if path:
+        write_parity_summary(path, RECORDS)
+
+
+def write_parity_summary(path, records):
+    """Worst figures per test (markdown table): the asserted metric of each
+    mode (bf16 NS: max |dO|; fp32 NS: relative Frobenius error) and the norm
+    ratio, over every matrix the test compared."""
+    groups = {}
+    for r in records:
+        groups.setdefault((r.get("test", ""), r.get("ns", "?"), r.get("variant", "?")), []).append(r)
+    lines = ["| test | NS | variant | matrices | worst max abs dO | worst rel F dO | worst abs(norm ratio - 1) |",
+             "|---|---|---|---:|---:|---:|---:|"]
+    for (test, ns, variant), rs in groups.items():
+        lines.append(f"| `{test.split('::', 1)[-1]}` ({test.split('::', 1)[0].split('/')[-1]}) | {ns} | {variant} | "
+                     f"{len(rs)} | {max(r['max_abs_dO'] for r in rs):.2e} | {max(r['rel_F_dO'] for r in rs):.2e} | "
+                     f"{max(abs(r['norm_ratio_m1']) for r in rs):.2e} |")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")

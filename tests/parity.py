@@ -4,6 +4,7 @@ through the float64 oracle on the same inputs, and compare."""
 from __future__ import annotations
 
 from dataclasses import dataclass
+import os
 from typing import List, Optional
 
 import numpy as np
@@ -119,7 +120,8 @@ def check_matrix(gpu: GpuResult, ref, i: int, cfg, variant: str, wl, scale: floa
     raw = float(np.max(np.abs(o_g - o_r))) if o_g.size else 0.0
     rel = float(np.linalg.norm(o_g - o_r) / n_ref) if n_ref > 0 else float(np.linalg.norm(o_g))
     rec = {"case": f"{wl.name} {ctx}", "max_abs_dO": raw, "rel_F_dO": rel, "norm_ratio_m1": norm_ratio,
-           "max_abs_O": float(np.max(np.abs(o_r))) if o_r.size else 0.0}
+           "max_abs_O": float(np.max(np.abs(o_r))) if o_r.size else 0.0, "ns": cfg.ns_dtype,
+           "variant": variant, "test": os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]}
     if cfg.ns_dtype == "bf16":
         if variant == "dimuon":
             # Diagnostic only: the error with the oracle's post-scale s and

@@ -5,6 +5,7 @@ Inputs come from the seeded generators in ``workloads``; expected values
 come only from ``oracle``."""
 
 import ctypes
+import os
 import sys
 
 import numpy as np
@@ -232,7 +233,8 @@ def test_square_closed_form_from_zero_momentum(variant):
           f"max|O| {np.abs(expect).max():.3f}", flush=True)
     RECORDS.append({"case": f"closed form U f5(sigma) V^T {n}x{n} ({variant})", "max_abs_dO": err, "rel_F_dO": rel,
                     "norm_ratio_m1": float(np.linalg.norm(o) / np.linalg.norm(expect) - 1.0),
-                    "max_abs_O": float(np.abs(expect).max())})
+                    "max_abs_O": float(np.abs(expect).max()), "ns": cfg.ns_dtype, "variant": variant,
+                    "test": os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]})
     assert err <= 2e-2, err
     np.testing.assert_array_equal(gpu.m[0], to64(wl.mats[0].g))   # M = mu * 0 + G exactly
 
