@@ -45,23 +45,22 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
 # The same counters for the combine kernel of the GEMM workloads (one
 # iteration before the last, on the tiles those iterations use; a product
-# with a tail launch lists both launches), plus the matrix-core counters of that kernel: bf16 MFMA busy
-# cycles over the active cycles of the 1024 SIMDs (GRBM_GUI_ACTIVE summed
-# over the 8 XCDs, divided by 8), and the clock those active cycles imply.
-# Valid only for the GEMM and planner sources they were taken on; figures
-# and commands in profiles/gemm_counters_gpt2_square_moe.md (the square set
-# was counted on N(0,1) inputs of the same shapes: the readings do not
-# depend on the values).
+# with a tail launch lists both launches), plus the matrix-core counters of
+# that kernel: bf16 MFMA busy cycles over the active cycles of the 1024 SIMDs
+# (GRBM_GUI_ACTIVE summed over the 8 XCDs, divided by 8), and the clock those
+# active cycles imply.  Each workload was counted on its own inputs.  Valid
+# only for the GEMM and planner sources they were taken on; figures and
+# commands in profiles/gemm_counters_gpt2_square_moe.md.
 GEMM_SOURCES = ("dimuon_newton_schulz_amd/csrc/gemm_kernels.hip", "dimuon_newton_schulz_amd/csrc/api.hip",
                 "dimuon_newton_schulz_amd/csrc/common.h")
 MEASURED_GEMM = {
-    "sources_sha256": "e08ef813afd1849231c2a52aa26093e59315315747a2a79a42ab4503071e0edd",
-    "gpt2_small_12x4_bf16": {"fetch_kib": [134169.8, 5246.8], "write_kib": [163840.0, 2048.0],
-                             "mfma_busy_frac": 0.359, "clock_ghz": 2.19},
-    "square_8x4096x4096_bf16": {"fetch_kib": [786680.8], "write_kib": [262144.0],
-                                "mfma_busy_frac": 0.539, "clock_ghz": 1.92},
-    "moe_64x(2048x1408+1408x2048)_bf16": {"fetch_kib": [991409.2], "write_kib": [786432.4],
-                                          "mfma_busy_frac": 0.455, "clock_ghz": 2.02},
+    "sources_sha256": "8878f4c93b35fb31ebc4cc941e28f88d3126f8995a92aa1d1b0d3aa5ad2af12d",
+    "gpt2_small_12x4_bf16": {"fetch_kib": [134324.8, 5246.8], "write_kib": [163840.0, 2048.0],
+                             "mfma_busy_frac": 0.365, "clock_ghz": 2.13},
+    "square_8x4096x4096_bf16": {"fetch_kib": [786712.0], "write_kib": [262145.2],
+                                "mfma_busy_frac": 0.572, "clock_ghz": 1.93},
+    "moe_64x(2048x1408+1408x2048)_bf16": {"fetch_kib": [992042.3], "write_kib": [786444.1],
+                                          "mfma_busy_frac": 0.469, "clock_ghz": 1.95},
 }
 
 
