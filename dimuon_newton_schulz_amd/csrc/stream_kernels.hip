@@ -248,8 +248,10 @@ __global__ __launch_bounds__(256) void k_cond_factor(StepArgs a, const Tile* __r
 // ---------------------------------------------------------------------------
 template <bool ENERGIES>
 __global__ __launch_bounds__(256) void k_prescale(StepArgs a, const Tile* __restrict__ tiles, int out_parity) {
+  // The energy partials stage their squares in tileS before Y goes there
+  // (block_energies ends with a barrier after its last read of them): 17 KB
+  // less LDS per workgroup, eight workgroups per CU instead of four.
   __shared__ float tileS[64][65];
-  __shared__ float pS[ENERGIES ? 64 : 1][65];
   __shared__ float part[ENERGIES ? 4 : 1][64];
   __shared__ float red[4];
   const Tile t = tiles[blockIdx.x];
@@ -312,7 +314,7 @@ __global__ __launch_bounds__(256) void k_prescale(StepArgs a, const Tile* __rest
       }
     }
     if constexpr (ENERGIES)
-      block_energies(sq, si0, sj0, d, reinterpret_cast<float*>(a.ws + d.ge_off[out_parity]), pS, part);
+      block_energies(sq, si0, sj0, d, reinterpret_cast<float*>(a.ws + d.ge_off[out_parity]), tileS, part);
 #pragma unroll
     for (int e = 0; e < 16; ++e) tileS[r][c0 + e] = round_to(v[e], a.ns_dt);
   }
