@@ -397,6 +397,29 @@ def test_matrices_independent_of_batch(variant):
 
 
 @pytest.mark.parametrize("variant", ["muon", "dimuon"])
+def test_round_interleave_bit_identical(variant):
+    # A batch of one shape whose one-per-CU tile lists fill whole rounds on
+    # all XCDs (8 x 2048^2: 512 combine tiles, 256 symmetric ones after the
+    # tail split) has its rounds dealt across the XCDs; a matrix stepped alone
+    # keeps the plain order.  Tile order changes no arithmetic: bit for bit.
+    shapes = [(2048, 2048)] * 8
+    wl = W.random_batch(shapes, dtype="bf16", ns_dtype="bf16", seed=41, variant=variant)
+    cfg = cfg_of(wl)
+    fn = D.dimuon_step if variant == "dimuon" else D.muon_step
+    announce(f"round interleave {variant}")
+    together = _batch_params(wl, range(wl.count))
+    fn(together, cfg)
+    for i in (0, 5):
+        alone = _batch_params(wl, [i])
+        fn(alone, cfg)
+        torch.cuda.synchronize()
+        for name in ("w", "mom", "o_out"):
+            np.testing.assert_array_equal(getattr(alone[0], name).float().cpu().numpy(),
+                                          getattr(together[i], name).float().cpu().numpy(),
+                                          err_msg=f"matrix {i} {name}")
+
+
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
 def test_nonfinite_gradient_stays_in_its_matrix(variant):
     # NaN propagates as IEEE arithmetic does (no status word): a NaN in one
     # element of a gradient gives a NaN in that element of M_t and a
