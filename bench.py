@@ -432,6 +432,14 @@ def toy_report(dev):
     return out
 
 
+_T0 = time.perf_counter()
+
+
+def progress(msg):
+    """One line per phase on stderr (stdout carries only the JSON line)."""
+    print(f"[bench {time.perf_counter() - _T0:6.1f} s] {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -452,9 +460,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     variant = args.variant or ("muon" if args.config == "c3" else "dimuon")
+    progress(f"building {args.config} ({variant})")
     wl = make_workload(args.config, dev, variant)
     work = algorithmic(wl, is_thin)
     full_count = wl.count
+    progress(f"timing {wl.name}: {args.warmup} warmup + {args.steps} steps")
     cfg, ms, per_kind, overhead, sets, per_set = measure(wl, args.steps, args.warmup, args.sets, graph=args.graph)
     kind, roof = roofline_for(wl, cfg, per_kind, work, args.steps)
     total_flops = 5 * (work["gram_flops"] + work["poly_flops"] + work["comb_flops"])
@@ -501,6 +511,7 @@ def main():
     if args.extra != "none":
         for item in args.extra.split(","):
             name, _, var = item.partition(":")
+            progress(f"building and timing {item}")
             wl2 = make_workload(name, dev, var or None)
             w2 = algorithmic(wl2, is_thin)
             cfg2, ms2, pk2, _, sets2, _ = measure(wl2, args.extra_steps, 2, args.sets, graph=args.graph)
@@ -517,9 +528,11 @@ def main():
             del wl2
             torch.cuda.empty_cache()
     if not args.no_toy:
+        progress("toy report")
         out["toy_report"] = toy_report(dev)
 
     if not args.no_cpu_baseline:
+        progress("oracle on the host cores")
         out["cpu_baseline"] = cpu_baseline(host_sample(args.config, variant), full_count, args.cpu_seconds)
         # Single-thread figures for the two small configurations.
         single = {}
@@ -536,6 +549,7 @@ def main():
                 continue
             key = (name, rec["variant"])
             if key not in samples:
+                progress(f"oracle on one matrix of each shape of {name}")
                 samples[key] = cpu_baseline(host_sample(name, rec["variant"]), counts[name], 0.0)
             rec["cpu_baseline"] = samples[key]
     out["workloads"] = [rec for _, rec in extras]
