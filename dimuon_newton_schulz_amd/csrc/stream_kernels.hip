@@ -250,7 +250,8 @@ template <bool ENERGIES>
 __global__ __launch_bounds__(256) void k_prescale(StepArgs a, const Tile* __restrict__ tiles, int out_parity) {
   // The energy partials stage their squares in tileS before Y goes there
   // (block_energies ends with a barrier after its last read of them): 17 KB
-  // less LDS per workgroup, eight workgroups per CU instead of four.
+  // less LDS per workgroup: seven waves per SIMD (register-bound) instead of
+  // four (LDS-bound).
   __shared__ float tileS[64][65];
   __shared__ float part[ENERGIES ? 4 : 1][64];
   __shared__ float red[4];
