@@ -12,7 +12,7 @@ import torch
 
 import dimuon_newton_schulz_amd as D
 import workloads as W
-from parity import check_matrix, run_oracle, to64, GpuResult
+from parity import check_matrix, run_gpu, run_oracle, to64, GpuResult
 
 pytestmark = pytest.mark.gpu
 
@@ -102,3 +102,20 @@ def test_fullsize_moe_dimuon():
     sample = [0, 1, 126, 127]              # up and down, first and last expert
     cfg, params, host = run_plan(wl, "dimuon", set(sample))
     compare(wl, "dimuon", cfg, params, host, sample)
+
+
+@pytest.mark.parametrize("variant", ["dimuon", "muon"])
+def test_fullsize_fp32_products(variant):
+    # The fp32 Newton-Schulz products at the largest shapes of the sets: one
+    # 4096^2 matrix of the square recipe and one MoE expert pair (2048 x 1408
+    # and 1408 x 2048), each within the fp32 bound of 1e-5 relative (measured
+    # 4.5e-6 and 3-4e-6).
+    for wl in (W.square_batch(count=1, n=4096, seed=3, device="cuda", variant=variant),
+               W.moe_experts(experts=1, device="cuda")):
+        cfg = D.StepConfig(lr=wl.lr, momentum=wl.mu, ns_steps=wl.ns_steps, w_dtype=wl.w_dtype,
+                           g_dtype=wl.g_dtype, mom_dtype=wl.mom_dtype, ns_dtype="f32")
+        announce(f"{wl.name} {variant}, fp32 products")
+        gpu = run_gpu(wl, variant, cfg)
+        for i in range(wl.count):
+            announce(f"oracle on matrix {i} {wl.mats[i].shape}")
+            check_matrix(gpu, run_oracle(wl, variant, cfg, i), i, cfg, variant, wl)
