@@ -110,6 +110,9 @@ def parse():
     ap.add_argument("--no-toy", action="store_true", help="skip the 4 x 16 toy's column-share report")
     ap.add_argument("--graph", action="store_true",
                     help="time the plans replaying their launch sequences as HIP graphs")
+    ap.add_argument("--next", action="store_true",
+                    help="turn on the extensions together: Nesterov input, decoupled weight decay 0.01, a "
+                         "per-iteration coefficient schedule and a per-matrix update scale of 0.5")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="bytes of a plain device-to-device copy run once before the workload "
                          "(calibrates HBM byte counters against a known size)")
@@ -183,17 +186,31 @@ ROTATION_TARGET_BYTES = 2 * 256 * 2 ** 20
 MAX_SETS = 64
 
 
-def measure(wl, steps, warmup, sets=0, ns_dtype=None, graph=False):
+# The extensions' settings for --next.  The schedule keeps the quintic's
+# coefficients for the first iterations and ends on the classical
+# Newton-Schulz quintic (15/8, -10/8, 3/8); the values only steer the
+# arithmetic, the cost is the same for any schedule.
+NEXT_SETTINGS = {"nesterov": True, "weight_decay": 0.01, "update_scale": 0.5,
+                 "coeff_schedule": [(3.4445, -4.7750, 2.0315)] * 4 + [(1.875, -1.25, 0.375)]}
+
+
+def measure(wl, steps, warmup, sets=0, ns_dtype=None, graph=False, next_features=False):
     import torch
     import dimuon_newton_schulz_amd as D
 
     cfg = D.StepConfig(lr=wl.lr, momentum=wl.mu, ns_steps=wl.ns_steps, w_dtype=wl.w_dtype,
                        g_dtype=wl.g_dtype, mom_dtype=wl.mom_dtype, ns_dtype=ns_dtype or wl.ns_dtype)
+    scale = 1.0
+    if next_features:
+        cfg.nesterov = NEXT_SETTINGS["nesterov"]
+        cfg.weight_decay = NEXT_SETTINGS["weight_decay"]
+        cfg.coeff_schedule = NEXT_SETTINGS["coeff_schedule"][:wl.ns_steps]
+        scale = NEXT_SETTINGS["update_scale"]
     dimuon = wl.variant == "dimuon"
     plans = []
 
     def new_plan():
-        params = [D.Param(w=m.w.clone(), g=m.g.clone(), mom=m.m_prev.clone()) for m in wl.mats]
+        params = [D.Param(w=m.w.clone(), g=m.g.clone(), mom=m.m_prev.clone(), update_scale=scale) for m in wl.mats]
         plans.append(D.Plan(params, cfg, dimuon=dimuon))
 
     new_plan()
@@ -465,7 +482,8 @@ def main():
     work = algorithmic(wl, is_thin)
     full_count = wl.count
     progress(f"timing {wl.name}: {args.warmup} warmup + {args.steps} steps")
-    cfg, ms, per_kind, overhead, sets, per_set = measure(wl, args.steps, args.warmup, args.sets, graph=args.graph)
+    cfg, ms, per_kind, overhead, sets, per_set = measure(wl, args.steps, args.warmup, args.sets, graph=args.graph,
+                                                         next_features=args.next)
     kind, roof = roofline_for(wl, cfg, per_kind, work, args.steps)
     total_flops = 5 * (work["gram_flops"] + work["poly_flops"] + work["comb_flops"])
     dtype = "f32" if (wl.w_dtype == "f32" and all(is_thin(*m.shape) for m in wl.mats)) else cfg.ns_dtype
@@ -484,7 +502,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "variant": wl.variant, "matrices": wl.count,
                    "ns_dtype": cfg.ns_dtype, "ns_steps": cfg.ns_steps, "buffer_sets": sets,
-                   "launches": "hip graph" if args.graph else "stream", "parallelism": "single-gpu"},
+                   "launches": "hip graph" if args.graph else "stream", "parallelism": "single-gpu",
+                   **({"extensions": {k: (f"{len(v)} rows" if k == "coeff_schedule" else v)
+                                      for k, v in NEXT_SETTINGS.items()}} if args.next else {})},
         "matrices_per_s": round(wl.count * 1000.0 / ms, 1),
         "rotation_resident_bytes": sets * per_set,
         "step_gbs_algorithmic": round(work["hbm_bytes_min"] / (ms * 1e-3) / 1e9, 1),
@@ -514,7 +534,8 @@ def main():
             progress(f"building and timing {item}")
             wl2 = make_workload(name, dev, var or None)
             w2 = algorithmic(wl2, is_thin)
-            cfg2, ms2, pk2, _, sets2, _ = measure(wl2, args.extra_steps, 2, args.sets, graph=args.graph)
+            cfg2, ms2, pk2, _, sets2, _ = measure(wl2, args.extra_steps, 2, args.sets, graph=args.graph,
+                                                  next_features=args.next)
             k2, roof2 = roofline_for(wl2, cfg2, pk2, w2, args.extra_steps)
             tf = 5 * (w2["gram_flops"] + w2["poly_flops"] + w2["comb_flops"])
             rec = {"workload": wl2.name, "variant": wl2.variant, "matrices": wl2.count,
