@@ -54,13 +54,13 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 GEMM_SOURCES = ("dimuon_newton_schulz_amd/csrc/gemm_kernels.hip", "dimuon_newton_schulz_amd/csrc/api.hip",
                 "dimuon_newton_schulz_amd/csrc/common.h")
 MEASURED_GEMM = {
-    "sources_sha256": "8878f4c93b35fb31ebc4cc941e28f88d3126f8995a92aa1d1b0d3aa5ad2af12d",
-    "gpt2_small_12x4_bf16": {"fetch_kib": [134324.8, 5246.8], "write_kib": [163840.0, 2048.0],
-                             "mfma_busy_frac": 0.365, "clock_ghz": 2.13},
-    "square_8x4096x4096_bf16": {"fetch_kib": [786712.0], "write_kib": [262145.2],
-                                "mfma_busy_frac": 0.572, "clock_ghz": 1.93},
-    "moe_64x(2048x1408+1408x2048)_bf16": {"fetch_kib": [992042.3], "write_kib": [786444.1],
-                                          "mfma_busy_frac": 0.469, "clock_ghz": 1.95},
+    "sources_sha256": "a6a0ec28b2f3db2a98941910df8cdafa87eda0b34494622b4fd4b5b4f30509bf",
+    "gpt2_small_12x4_bf16": {"fetch_kib": [134426.0, 5246.8], "write_kib": [163840.1, 2048.0],
+                             "mfma_busy_frac": 0.357, "clock_ghz": 2.25},
+    "square_8x4096x4096_bf16": {"fetch_kib": [787120.6], "write_kib": [262199.5],
+                                "mfma_busy_frac": 0.570, "clock_ghz": 2.01},
+    "moe_64x(2048x1408+1408x2048)_bf16": {"fetch_kib": [960964.8], "write_kib": [786471.3],
+                                          "mfma_busy_frac": 0.467, "clock_ghz": 2.03},
 }
 
 

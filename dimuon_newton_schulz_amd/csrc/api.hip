@@ -184,13 +184,15 @@ size_t put(std::vector<unsigned char>& buf, size_t off, const std::vector<T>& v)
 // CU, the 128 x 128 kernel two.  For each product kind the batch takes the
 // big tiles where they fit, unless the estimated time with 128 x 128 tiles
 // everywhere is lower (few big tiles leave CUs idle in the last round).
-// Within a matrix, tiles are listed in groups of four tile rows, column by
-// column, so that the workgroups running at once share operand panels.
+// Within a matrix, tiles are listed in groups of tile rows, column by
+// column, so that the workgroups running at once share operand panels:
+// groups of two rows for the symmetric products and of eight for the
+// combine (against four for both: MoE step 0.8% faster, 8 x 4096^2 0.25%).
 constexpr int kCUs = 256;
 constexpr double kSmallTileEff = 0.6;   // 128 x 128 kernel efficiency relative to the big tiles
 
 void add_tiles(std::vector<Tile>& out, uint16_t mat, int rows, int cols, bool upper) {
-  constexpr int kGroup = 4;
+  const int kGroup = upper ? 2 : 8;
   for (int g0 = 0; g0 < rows; g0 += kGroup)
     for (int tj = 0; tj < cols; ++tj)
       for (int ti = g0; ti < std::min(rows, g0 + kGroup); ++ti)
