@@ -110,6 +110,8 @@ def parse():
     ap.add_argument("--no-toy", action="store_true", help="skip the 4 x 16 toy's column-share report")
     ap.add_argument("--graph", action="store_true",
                     help="time the plans replaying their launch sequences as HIP graphs")
+    ap.add_argument("--ns-dtype", default=None, choices=[None, "bf16", "f32"],
+                    help="precision of the Newton-Schulz products (default: the workload's)")
     ap.add_argument("--next", action="store_true",
                     help="turn on the extensions together: Nesterov input, decoupled weight decay 0.01, a "
                          "per-iteration coefficient schedule and a per-matrix update scale of 0.5")
@@ -325,7 +327,8 @@ def roofline_for(wl, cfg, per_kind, work, steps):
         out["flops_per_launch"] = flops
     else:
         out["flops_per_iteration"] = flops
-    counted = measured_gemm(wl.name.replace("_gaussian", "")) if kind == "combine" else None
+    # (The committed counter figures are those of the bf16 products.)
+    counted = measured_gemm(wl.name) if kind == "combine" and cfg.ns_dtype == "bf16" else None
     if counted is not None:
         out["traffic"] = counted["traffic"]
         if per_iter != 1:
@@ -482,8 +485,8 @@ def main():
     work = algorithmic(wl, is_thin)
     full_count = wl.count
     progress(f"timing {wl.name}: {args.warmup} warmup + {args.steps} steps")
-    cfg, ms, per_kind, overhead, sets, per_set = measure(wl, args.steps, args.warmup, args.sets, graph=args.graph,
-                                                         next_features=args.next)
+    cfg, ms, per_kind, overhead, sets, per_set = measure(wl, args.steps, args.warmup, args.sets, ns_dtype=args.ns_dtype,
+                                                         graph=args.graph, next_features=args.next)
     kind, roof = roofline_for(wl, cfg, per_kind, work, args.steps)
     total_flops = 5 * (work["gram_flops"] + work["poly_flops"] + work["comb_flops"])
     dtype = "f32" if (wl.w_dtype == "f32" and all(is_thin(*m.shape) for m in wl.mats)) else cfg.ns_dtype
@@ -534,8 +537,8 @@ def main():
             progress(f"building and timing {item}")
             wl2 = make_workload(name, dev, var or None)
             w2 = algorithmic(wl2, is_thin)
-            cfg2, ms2, pk2, _, sets2, _ = measure(wl2, args.extra_steps, 2, args.sets, graph=args.graph,
-                                                  next_features=args.next)
+            cfg2, ms2, pk2, _, sets2, _ = measure(wl2, args.extra_steps, 2, args.sets, ns_dtype=args.ns_dtype,
+                                                  graph=args.graph, next_features=args.next)
             k2, roof2 = roofline_for(wl2, cfg2, pk2, w2, args.extra_steps)
             tf = 5 * (w2["gram_flops"] + w2["poly_flops"] + w2["comb_flops"])
             rec = {"workload": wl2.name, "variant": wl2.variant, "matrices": wl2.count,

@@ -33,6 +33,7 @@ namespace muon {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int LBK = 64;        // k per pipeline stage: whole 128-byte lines of each operand row
 constexpr int NQ = LBK / 16;   // MFMA k-steps per stage
@@ -164,7 +165,7 @@ __device__ __forceinline__ void issue_stage(const MUON_GLOBAL uint16_t* P, int64
 // i mod 4 of the 8-byte reads of lanes 4 e + i / 4, e = 0..3, so lane m of the
 // group reads the four n-values 4 (m mod 4) .. + 3 of its 16-column half at
 // k-row 8 (l / 32) + m / 4, and four k-rows further down for the second read.
-template <int BM, int BN, bool QT>
+template <int BM, int BN, bool QT, bool F32 = false>
 __device__ __forceinline__ void mma_bf16(const uint16_t* Pg, int64_t ldp, const uint16_t* Qg, int64_t ldq, int K,
                                          uint16_t* b0, uint16_t* b1,
                                          f32x16_t (&acc)[GemmT<BM, BN>::MS][GemmT<BM, BN>::NS],
@@ -226,11 +227,27 @@ __device__ __forceinline__ void mma_bf16(const uint16_t* Pg, int64_t ldp, const 
       __builtin_amdgcn_s_setprio(1);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (F32) {
+      // fp32 operands: a lane's 16 bytes are 4 consecutive k of its row
+      // (k = 8q + 4 (lane >> 5) + 0..3 for chunk pair q); element e of both
+      // operands is the lane's k-slot of the e-th 32x32x2 product, so the
+      // four products cover the chunk pair's 8 k once each.
 #pragma unroll
-    for (int s = 0; s < MS; ++s)
+      for (int s = 0; s < MS; ++s)
 #pragma unroll
-      for (int t = 0; t < NS; ++t)
-        acc[s][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[s], rb[t], acc[s][t], 0, 0, 0);
+        for (int t = 0; t < NS; ++t) {
+          const f32x4_t a4 = __builtin_bit_cast(f32x4_t, ra[s]);
+          const f32x4_t b4 = __builtin_bit_cast(f32x4_t, rb[t]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[s][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[e], b4[e], acc[s][t], 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+      for (int s = 0; s < MS; ++s)
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+          acc[s][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[s], rb[t], acc[s][t], 0, 0, 0);
+    }
     if constexpr (QT) {
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(0);
@@ -381,7 +398,8 @@ __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[GemmT<BM, 
     constexpr int rd = rdc;
     float* st = stage(rd);
     auto row_of = [&](int il) { return (il / QR) * HM + rd * QR + il % QR; };
-    uint4 xt[CT], xn[CN];
+    decltype(aux_t(0, 0)) xt[CT];
+    decltype(aux_n(0, 0)) xn[CN];
     if (do_t)
       static_for<0, CT>([&](auto q) {
         int j, il;
@@ -643,148 +661,163 @@ __global__ __launch_bounds__((GemmT<BM, BN>::NT), 1) void k_combine_bf16(StepArg
 }
 
 // ---------------------------------------------------------------------------
-// fp32 path (ns dtype F32): the same products with IEEE fp32 multiply-adds.
-// 128 x 128 tile, 256 threads, each an 8 x 8 micro-tile; K in steps of 16.
+// fp32 path (ns dtype F32): the same products on the matrix cores in fp32
+// (v_mfma_f32_32x32x2f32: fp32 operands, fp32 accumulation), 128 x 128
+// tiles, four waves.  The main loop is the bf16 one: a stage holds 32 k
+// of each row (the same 128 bytes), and every 16-byte fragment read feeds
+// four products instead of one.  Both operands are read k-contiguous
+// ("NT"): the fp32 iterates keep X^T beside X, and the combine multiplies B
+// by rows of X^T.  The aX term stays in the combine (aX + BX).
 // ---------------------------------------------------------------------------
-constexpr int FBK = 16, FLD = 128 + 4, FT = 128;
+constexpr int FT = 128;
 
-__device__ __forceinline__ void mma_nt_f32(const float* __restrict__ Pg, int64_t ldp,
-                                           const float* __restrict__ Qg, int64_t ldq, int K,
-                                           float (*As)[FLD], float (*Bs)[FLD], float acc[8][8]) {
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  for (int k0 = 0; k0 < K; k0 += FBK) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int c = tid + 256 * q, row = c >> 2, k4 = (c & 3) * 4;
-      const float4 va = *reinterpret_cast<const float4*>(Pg + row * ldp + k0 + k4);
-      const float4 vb = *reinterpret_cast<const float4*>(Qg + row * ldq + k0 + k4);
-      As[k4 + 0][row] = va.x; As[k4 + 1][row] = va.y; As[k4 + 2][row] = va.z; As[k4 + 3][row] = va.w;
-      Bs[k4 + 0][row] = vb.x; Bs[k4 + 1][row] = vb.y; Bs[k4 + 2][row] = vb.z; Bs[k4 + 3][row] = vb.w;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < FBK; ++k) {
-      float av[8], bv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { av[e] = As[k][ty * 8 + e]; bv[e] = Bs[k][tx * 8 + e]; }
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[r][c] = __builtin_fmaf(av[r], bv[c], acc[r][c]);
-    }
-    __syncthreads();
-  }
+// Eight consecutive fp32 values.
+struct F8 {
+  float4 lo, hi;
+};
+__device__ __forceinline__ F8 fetch8_f32(const float* p, int64_t idx) {
+  const MUON_GLOBAL float4* q = reinterpret_cast<const MUON_GLOBAL float4*>(gmem(p) + idx);
+  return F8{q[0], q[1]};
+}
+__device__ __forceinline__ void unpack8_f32(const F8& u, float (&v)[8]) {
+  v[0] = u.lo.x; v[1] = u.lo.y; v[2] = u.lo.z; v[3] = u.lo.w;
+  v[4] = u.hi.x; v[5] = u.hi.y; v[6] = u.hi.z; v[7] = u.hi.w;
 }
 
-__global__ __launch_bounds__(256) void k_syrk_f32(StepArgs a, const Tile* __restrict__ tiles, int ntiles,
-                                                  int kind, int src_x, int first, Coeffs cf) {
-  __shared__ float As[FBK][FLD], Bs[FBK][FLD];
+// fp32 operands as the main loop's 16-bit units (two per float).
+__device__ __forceinline__ const uint16_t* units(const float* p) { return reinterpret_cast<const uint16_t*>(p); }
+
+template <int KIND>
+__global__ __launch_bounds__((GemmT<FT, FT>::NT), 1) void k_syrk_f32(StepArgs a, const Tile* __restrict__ tiles,
+                                                                   int ntiles, int src_x, int first, Coeffs cf) {
+  using G = GemmT<FT, FT>;
+  __shared__ typename G::Smem sm;
   const Tile t = tiles[xcd_remap(blockIdx.x, ntiles)];
   const MatDesc& d = a.desc[t.mat];
-  const float* P;
-  int64_t ld;
-  if (kind == 0) {
-    P = reinterpret_cast<const float*>(a.ws + d.x_off[2 * src_x]);
-    ld = d.NP;
-  } else {
-    P = reinterpret_cast<const float*>(a.ws + d.a_off);
-    ld = d.KP;
-  }
-  float acc[8][8] = {};
-  mma_nt_f32(P + static_cast<int64_t>(t.ti) * FT * ld, ld, P + static_cast<int64_t>(t.tj) * FT * ld, ld,
-             static_cast<int>(ld), As, Bs, acc);
-  const float alpha = (kind == 0) ? (first ? a.scal[d.scal_idx].inv_nu2 : 1.0f) : cf.c;
+  const float* P = reinterpret_cast<const float*>(a.ws + (KIND == 0 ? d.x_off[2 * src_x] : d.a_off));
+  const int64_t ld = KIND == 0 ? d.NP : d.KP;
+  f32x16_t acc[G::MS][G::NS];
+#pragma unroll
+  for (int s = 0; s < G::MS; ++s)
+#pragma unroll
+    for (int u = 0; u < G::NS; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[s][u][r] = 0.0f;
+  mma_bf16<FT, FT, false, true>(units(P + static_cast<int64_t>(t.ti) * FT * ld), 2 * ld,
+                                units(P + static_cast<int64_t>(t.tj) * FT * ld), 2 * ld, static_cast<int>(2 * ld),
+                                sm.buf[0], sm.buf[1], acc, t.ti == t.tj);
+
+  // Gram: A = X X^T / nu^2 on the first iteration; polynomial: c (A A) + b A.
+  const float alpha = (KIND == 0) ? (first ? a.scal[d.scal_idx].inv_nu2 : 1.0f) : cf.c;
   const float* E = reinterpret_cast<const float*>(a.ws + d.a_off);
-  float* C = reinterpret_cast<float*>(a.ws + (kind == 0 ? d.a_off : d.b_off));
-  const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
-  const int64_t gi0 = static_cast<int64_t>(t.ti) * FT + ty * 8, gj0 = static_cast<int64_t>(t.tj) * FT + tx * 8;
-  float v[8][8];
+  void* dst = a.ws + (KIND == 0 ? d.a_off : d.b_off);
+  const int64_t gi0 = static_cast<int64_t>(t.ti) * FT, gj0 = static_cast<int64_t>(t.tj) * FT;
+  const int64_t ldo = d.KP;
+  auto aux_t = [&](int j, int i0) { return KIND == 1 ? fetch8_f32(E, (gj0 + j) * ldo + gi0 + i0) : F8{}; };
+  auto aux_n = [&](int i, int j0) { return KIND == 1 ? fetch8_f32(E, (gi0 + i) * ldo + gj0 + j0) : F8{}; };
+  auto fin = [&](float (&v)[8], const F8& aux) {
+    float e8[8];
+    unpack8_f32(aux, e8);
 #pragma unroll
-  for (int r = 0; r < 8; ++r)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      v[r][c] = alpha * acc[r][c];
-      if (kind == 1) v[r][c] = v[r][c] + cf.b * E[(gi0 + r) * d.KP + gj0 + c];
-    }
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    float4* q = reinterpret_cast<float4*>(C + (gi0 + r) * d.KP + gj0);
-    q[0] = make_float4(v[r][0], v[r][1], v[r][2], v[r][3]);
-    q[1] = make_float4(v[r][4], v[r][5], v[r][6], v[r][7]);
-  }
-  if (t.ti != t.tj) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float4* q = reinterpret_cast<float4*>(C + (gj0 + c) * d.KP + gi0);
-      q[0] = make_float4(v[0][c], v[1][c], v[2][c], v[3][c]);
-      q[1] = make_float4(v[4][c], v[5][c], v[6][c], v[7][c]);
-    }
-  }
+    for (int e = 0; e < 8; ++e) v[e] = KIND == 1 ? alpha * v[e] + cf.b * e8[e] : alpha * v[e];
+  };
+  auto out_t = [&](int j, int i0, float (&v)[8], const F8& aux) {
+    fin(v, aux);
+    store8(dst, (gj0 + j) * ldo + gi0 + i0, DT_F32, v);
+  };
+  auto out_n = [&](int i, int j0, float (&v)[8], const F8& aux) {
+    fin(v, aux);
+    store8(dst, (gi0 + i) * ldo + gj0 + j0, DT_F32, v);
+  };
+  staged_epilogue<FT, FT, 2, false>(acc, [&](int) { return sm.st; }, true, t.ti != t.tj, aux_t, aux_n, out_t, out_n);
 }
 
-__global__ __launch_bounds__(256) void k_combine_f32(StepArgs a, const Tile* __restrict__ tiles, int ntiles,
-                                                     int src_x, int dst_x, int first, int last, int product,
-                                                     Coeffs cf) {
-  __shared__ float As[FBK][FLD], Bs[FBK][FLD];
-  __shared__ float red[4];
+// X' = alpha (a X + B X) (product = 0: alpha a X).  Writes X' and X'^T while
+// iterating; on the last iteration Z in the caller's orientation and
+// Dimuon's norm partials, one pair per 128 x 128 tile.
+template <bool LAST>
+__global__ __launch_bounds__((GemmT<FT, FT>::NT), 1) void k_combine_f32(StepArgs a, const Tile* __restrict__ tiles,
+                                                                      int ntiles, int src_x, int dst_x, int first,
+                                                                      int product, Coeffs cf) {
+  using G = GemmT<FT, FT>;
+  __shared__ typename G::Smem sm;
+  __shared__ float red[G::NW];
   const Tile t = tiles[xcd_remap(blockIdx.x, ntiles)];
   const MatDesc& d = a.desc[t.mat];
   const float* Bm = reinterpret_cast<const float*>(a.ws + d.b_off);
   const float* X = reinterpret_cast<const float*>(a.ws + d.x_off[2 * src_x]);
   const float* XT = reinterpret_cast<const float*>(a.ws + d.x_off[2 * src_x + 1]);
-  float acc[8][8] = {};
+  const int64_t gi0 = static_cast<int64_t>(t.ti) * FT, gj0 = static_cast<int64_t>(t.tj) * FT;
+  f32x16_t acc[G::MS][G::NS];
+#pragma unroll
+  for (int s = 0; s < G::MS; ++s)
+#pragma unroll
+    for (int u = 0; u < G::NS; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[s][u][r] = 0.0f;
+  // B X: rows of B against rows of X^T (both k-contiguous, K = KP).
   if (product)
-    mma_nt_f32(Bm + static_cast<int64_t>(t.ti) * FT * d.KP, d.KP, XT + static_cast<int64_t>(t.tj) * FT * d.KP,
-               d.KP, d.KP, As, Bs, acc);
+    mma_bf16<FT, FT, false, true>(units(Bm + gi0 * d.KP), 2 * d.KP, units(XT + gj0 * d.KP), 2 * d.KP,
+                                  static_cast<int>(2 * d.KP), sm.buf[0], sm.buf[1], acc, false);
+
   const float alpha = first ? a.scal[d.scal_idx].inv_nu : 1.0f;
-  const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
-  const int64_t gi0 = static_cast<int64_t>(t.ti) * FT + ty * 8, gj0 = static_cast<int64_t>(t.tj) * FT + tx * 8;
-  const bool partials = last && a.dimuon;
-  const float* dgr = reinterpret_cast<const float*>(a.ws + (d.tall ? d.dc_off : d.dr_off));
-  const float* dgc = reinterpret_cast<const float*>(a.ws + (d.tall ? d.dr_off : d.dc_off));
-  float v[8][8];
+  const bool partials = LAST && a.dimuon;
+  const MUON_GLOBAL float* dgr = gmem(reinterpret_cast<const float*>(a.ws + (d.tall ? d.dc_off : d.dr_off)));
+  const MUON_GLOBAL float* dgc = gmem(reinterpret_cast<const float*>(a.ws + (d.tall ? d.dr_off : d.dc_off)));
+  void* dst_n = LAST ? (d.tall ? nullptr : a.ws + d.z_off) : a.ws + d.x_off[2 * dst_x];
+  void* dst_t = LAST ? (d.tall ? a.ws + d.z_off : nullptr) : a.ws + d.x_off[2 * dst_x + 1];
   float sz = 0.0f, sp = 0.0f;
+  // Row runs read X, column runs X^T: the a X term of each element.
+  auto aux_t = [&](int j, int i0) { return fetch8_f32(XT, (gj0 + j) * d.KP + gi0 + i0); };
+  auto aux_n = [&](int i, int j0) { return fetch8_f32(X, (gi0 + i) * d.NP + gj0 + j0); };
+  auto fin = [&](float (&v)[8], const F8& aux) {
+    float x[8];
+    unpack8_f32(aux, x);
 #pragma unroll
-  for (int r = 0; r < 8; ++r)
+    for (int e = 0; e < 8; ++e) v[e] = alpha * (cf.a * x[e] + v[e]);
+  };
+  auto factors8 = [&](const MUON_GLOBAL float* f, int64_t at, float (&r)[8]) {
+    const float4 lo = *reinterpret_cast<const MUON_GLOBAL float4*>(f + at);
+    const float4 hi = *reinterpret_cast<const MUON_GLOBAL float4*>(f + at + 4);
+    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+  };
+  auto accum = [&](float fr, float v, float fc) {
+    const float p = (fr * v) * fc;
+    sz = sz + v * v;
+    sp = sp + p * p;
+  };
+  // On the last iteration each element is stored once: the row run when the
+  // caller's matrix is wide, the column run when it is tall; its partials
+  // are summed there.
+  auto out_t = [&](int j, int i0, float (&v)[8], const F8& aux) {
+    fin(v, aux);
+    if (LAST && partials) {
+      float fr[8];
+      factors8(dgr, gi0 + i0, fr);
+      const float fc = dgc[gj0 + j];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const float x = X[(gi0 + r) * d.NP + gj0 + c];
-      v[r][c] = alpha * (cf.a * x + acc[r][c]);
-      if (partials) {
-        const int64_t gi = gi0 + r, gj = gj0 + c;
-        const float fr = gi < d.k ? dgr[gi] : 0.0f;
-        const float fc = gj < d.N ? dgc[gj] : 0.0f;
-        const float p = (fr * v[r][c]) * fc;
-        sz = sz + v[r][c] * v[r][c];
-        sp = sp + p * p;
-      }
+      for (int e = 0; e < 8; ++e) accum(fr[e], v[e], fc);
     }
-  float* Xn = reinterpret_cast<float*>(a.ws + d.x_off[2 * dst_x]);
-  float* XnT = reinterpret_cast<float*>(a.ws + d.x_off[2 * dst_x + 1]);
-  float* Z = reinterpret_cast<float*>(a.ws + d.z_off);
-  const bool write_n = !last || !d.tall;
-  const bool write_t = !last || d.tall;
-  float* dn = last ? Z : Xn;
-  float* dt = last ? Z : XnT;
-  if (write_n) {
+    store8(dst_t, (gj0 + j) * d.KP + gi0 + i0, DT_F32, v);
+  };
+  auto out_n = [&](int i, int j0, float (&v)[8], const F8& aux) {
+    fin(v, aux);
+    if (LAST && partials) {
+      float fc[8];
+      factors8(dgc, gj0 + j0, fc);
+      const float fr = dgr[gi0 + i];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      float4* q = reinterpret_cast<float4*>(dn + (gi0 + r) * d.NP + gj0);
-      q[0] = make_float4(v[r][0], v[r][1], v[r][2], v[r][3]);
-      q[1] = make_float4(v[r][4], v[r][5], v[r][6], v[r][7]);
+      for (int e = 0; e < 8; ++e) accum(fr, v[e], fc[e]);
     }
-  }
-  if (write_t) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float4* q = reinterpret_cast<float4*>(dt + (gj0 + c) * d.KP + gi0);
-      q[0] = make_float4(v[0][c], v[1][c], v[2][c], v[3][c]);
-      q[1] = make_float4(v[4][c], v[5][c], v[6][c], v[7][c]);
-    }
-  }
-  if (partials) {
-    sz = block_sum<4>(sz, red);
-    sp = block_sum<4>(sp, red);
+    store8(dst_n, (gi0 + i) * d.NP + gj0 + j0, DT_F32, v);
+  };
+  staged_epilogue<FT, FT, 2, false>(acc, [&](int) { return sm.st; }, dst_t != nullptr, dst_n != nullptr, aux_t,
+                                    aux_n, out_t, out_n);
+  if (LAST && partials) {
+    __syncthreads();
+    sz = block_sum<G::NW>(sz, red);
+    sp = block_sum<G::NW>(sp, red);
     if (threadIdx.x == 0) {
       float* pz = reinterpret_cast<float*>(a.ws + d.pz_off);
       const int idx = t.ti * (d.NP / FT) + t.tj;
@@ -802,8 +835,11 @@ hipError_t launch_syrk(const StepArgs& a, const Tile* tiles, int n, int bt, int 
   if (n <= 0) return hipSuccess;
   const int f = first ? 1 : 0;
   if (a.ns_dt != DT_BF16) {
-    if (bt != 128) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_syrk_f32, dim3(n), dim3(256), 0, s, a, tiles, n, kind, src_x, f, cf);
+    if (bt != FT) return hipErrorInvalidValue;
+    if (kind == 0)
+      hipLaunchKernelGGL(k_syrk_f32<0>, dim3(n), dim3(GemmT<FT, FT>::NT), 0, s, a, tiles, n, src_x, f, cf);
+    else
+      hipLaunchKernelGGL(k_syrk_f32<1>, dim3(n), dim3(GemmT<FT, FT>::NT), 0, s, a, tiles, n, src_x, f, cf);
     return hipGetLastError();
   }
 #define MUON_SYRK(BT, K) \
@@ -824,8 +860,11 @@ hipError_t launch_combine(const StepArgs& a, const Tile* tiles, int n, int bm, i
   if (n <= 0) return hipSuccess;
   const int f = first ? 1 : 0, l = last ? 1 : 0, p = product ? 1 : 0;
   if (a.ns_dt != DT_BF16) {
-    if (bm != 128 || bn != 128) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_combine_f32, dim3(n), dim3(256), 0, s, a, tiles, n, src_x, dst_x, f, l, p, cf);
+    if (bm != FT || bn != FT) return hipErrorInvalidValue;
+    if (last)
+      hipLaunchKernelGGL(k_combine_f32<true>, dim3(n), dim3(GemmT<FT, FT>::NT), 0, s, a, tiles, n, src_x, dst_x, f, p, cf);
+    else
+      hipLaunchKernelGGL(k_combine_f32<false>, dim3(n), dim3(GemmT<FT, FT>::NT), 0, s, a, tiles, n, src_x, dst_x, f, p, cf);
     return hipGetLastError();
   }
 #define MUON_COMB(BM, BN)                                                                                   \
