@@ -99,8 +99,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--variant", default=None, choices=[None, "muon", "dimuon"])
-    ap.add_argument("--extra", default="c3:muon,c4:dimuon,c4:muon,c5:dimuon",
-                    help="comma list of config:variant measured besides the main one, or 'none'")
+    ap.add_argument("--extra", default="c3:muon,c4:dimuon,c4:muon,c5:dimuon,c4:muon:f32",
+                    help="comma list of config:variant[:ns dtype] measured besides the main one, or 'none'")
     ap.add_argument("--extra-steps", type=int, default=10)
     ap.add_argument("--sets", type=int, default=0,
                     help="buffer sets rotated (0: automatic, enough that the rotation's resident bytes "
@@ -533,15 +533,15 @@ def main():
     extras = []
     if args.extra != "none":
         for item in args.extra.split(","):
-            name, _, var = item.partition(":")
+            name, var, ns = (item.split(":") + ["", ""])[:3]
             progress(f"building and timing {item}")
             wl2 = make_workload(name, dev, var or None)
             w2 = algorithmic(wl2, is_thin)
-            cfg2, ms2, pk2, _, sets2, _ = measure(wl2, args.extra_steps, 2, args.sets, ns_dtype=args.ns_dtype,
+            cfg2, ms2, pk2, _, sets2, _ = measure(wl2, args.extra_steps, 2, args.sets, ns_dtype=ns or args.ns_dtype,
                                                   graph=args.graph, next_features=args.next)
             k2, roof2 = roofline_for(wl2, cfg2, pk2, w2, args.extra_steps)
             tf = 5 * (w2["gram_flops"] + w2["poly_flops"] + w2["comb_flops"])
-            rec = {"workload": wl2.name, "variant": wl2.variant, "matrices": wl2.count,
+            rec = {"workload": wl2.name, "variant": wl2.variant, "ns_dtype": cfg2.ns_dtype, "matrices": wl2.count,
                    "steps": args.extra_steps, "buffer_sets": sets2, "ms_per_step": round(ms2, 4),
                    "steps_per_s": round(1000.0 / ms2, 3),
                    "matrices_per_s": round(wl2.count * 1000.0 / ms2, 1),
