@@ -53,9 +53,10 @@ constexpr int NQ = LBK / 16;   // MFMA k-steps per stage
 #ifndef MUON_GEMM_WC_SMALL
 #define MUON_GEMM_WC_SMALL 2
 #endif
-template <int BM, int BN>
+// WCX, when non-zero, sets the wave columns of a kernel apart from the rule.
+template <int BM, int BN, int WCX = 0>
 struct GemmT {
-  static constexpr int WC = BM * BN >= 32768 ? MUON_GEMM_WC_LARGE : MUON_GEMM_WC_SMALL;
+  static constexpr int WC = WCX ? WCX : (BM * BN >= 32768 ? MUON_GEMM_WC_LARGE : MUON_GEMM_WC_SMALL);
   static constexpr int NW = 2 * WC, NT = 64 * NW;    // waves, threads
   static constexpr int MS = BM / 64, NS = BN / (32 * WC);   // 32 x 32 blocks per wave
   static constexpr int LA = BM * 8 / NT, LB = BN * 8 / NT;  // 16-byte LDS loads per thread and stage
@@ -117,10 +118,10 @@ __device__ __forceinline__ int qswz(int row) { return 4 * (row & 3); }
 // same: Q is P (a diagonal tile of a symmetric product); only P's rows are
 // loaded, and the fragments of both operands come from them.
 // Loads Q0 .. Q1-1 of the thread's LA + LB (all of them by default).
-template <int BM, int BN, bool QT, int Q0 = 0, int Q1 = GemmT<BM, BN>::LPS>
+template <int BM, int BN, bool QT, int Q0 = 0, int Q1 = GemmT<BM, BN>::LPS, int WCX = 0>
 __device__ __forceinline__ void issue_stage(const MUON_GLOBAL uint16_t* P, int64_t ldp, const MUON_GLOBAL uint16_t* Q,
                                             int64_t ldq, int st, uint16_t* buf, bool same = false) {
-  using G = GemmT<BM, BN>;
+  using G = GemmT<BM, BN, WCX>;
   constexpr int LPR = BN / 8, RPI = 64 / LPR;   // k-major Q: lanes per k-row, k-rows per load
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int k0 = st * LBK;
@@ -165,12 +166,12 @@ __device__ __forceinline__ void issue_stage(const MUON_GLOBAL uint16_t* P, int64
 // i mod 4 of the 8-byte reads of lanes 4 e + i / 4, e = 0..3, so lane m of the
 // group reads the four n-values 4 (m mod 4) .. + 3 of its 16-column half at
 // k-row 8 (l / 32) + m / 4, and four k-rows further down for the second read.
-template <int BM, int BN, bool QT, bool F32 = false>
+template <int BM, int BN, bool QT, bool F32 = false, int WCX = 0>
 __device__ __forceinline__ void mma_bf16(const uint16_t* Pg, int64_t ldp, const uint16_t* Qg, int64_t ldq, int K,
                                          uint16_t* b0, uint16_t* b1,
-                                         f32x16_t (&acc)[GemmT<BM, BN>::MS][GemmT<BM, BN>::NS],
+                                         f32x16_t (&acc)[GemmT<BM, BN, WCX>::MS][GemmT<BM, BN, WCX>::NS],
                                          bool same = false) {
-  using G = GemmT<BM, BN>;
+  using G = GemmT<BM, BN, WCX>;
   constexpr int MS = G::MS, NS = G::NS, LPS = G::LPS, WN = BN / G::WC;
   static_assert(NQ % 2 == 0, "fragment sets alternate");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -180,9 +181,9 @@ __device__ __forceinline__ void mma_bf16(const uint16_t* Pg, int64_t ldp, const 
   const int nk = K / LBK;
   // Every wave's stage-0 loads are issued before any stage-1 load (the
   // barrier waits for issue, not for data): the first stage arrives first.
-  issue_stage<BM, BN, QT>(P, ldp, Q, ldq, 0, b0, same);
+  issue_stage<BM, BN, QT, 0, G::LPS, WCX>(P, ldp, Q, ldq, 0, b0, same);
   __builtin_amdgcn_s_barrier();
-  issue_stage<BM, BN, QT>(P, ldp, Q, ldq, 1, b1, same);
+  issue_stage<BM, BN, QT, 0, G::LPS, WCX>(P, ldp, Q, ldq, 1, b1, same);
   // Fragment addresses (elements within a stage): row (lane & 31) of each
   // 32-row block, logical chunk 2 q + (lane >> 5) for k-step q.  The swizzle
   // of a row depends on its index mod 16 only, i.e. on lane & 31.
@@ -275,10 +276,10 @@ __device__ __forceinline__ void mma_bf16(const uint16_t* Pg, int64_t ldp, const 
   // in a run of load issues while the matrix core idles (1.4% faster on the
   // 4096^2 set than all loads first).
   auto half_step = [&](uint16_t* cur, uint16_t* nxt, int kt) {
-    if (kt + 2 < nk) issue_stage<BM, BN, QT, 0, LPS / 2>(P, ldp, Q, ldq, kt + 2, cur, same);
+    if (kt + 2 < nk) issue_stage<BM, BN, QT, 0, LPS / 2, WCX>(P, ldp, Q, ldq, kt + 2, cur, same);
     read_step(nxt, 0, fa[0], fb[0]);
     mfma_step(fa[(NQ - 1) & 1], fb[(NQ - 1) & 1]);
-    if (kt + 2 < nk) issue_stage<BM, BN, QT, LPS / 2, LPS>(P, ldp, Q, ldq, kt + 2, cur, same);
+    if (kt + 2 < nk) issue_stage<BM, BN, QT, LPS / 2, LPS, WCX>(P, ldp, Q, ldq, kt + 2, cur, same);
 #pragma unroll
     for (int q = 1; q < NQ; ++q) {
       read_step(nxt, q, fa[q & 1], fb[q & 1]);
@@ -319,9 +320,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // Tile-relative column of block t for this lane (rows of a block's
 // accumulator group g are 8g + 4 (lane >> 5) + 0..3).
-template <int BM, int BN>
+template <int BM, int BN, int WCX = 0>
 __device__ __forceinline__ int blk_col(int t) {
-  using G = GemmT<BM, BN>;
+  using G = GemmT<BM, BN, WCX>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   return (wave % G::WC) * (BN / G::WC) + t * 32 + (lane & 31);
 }
@@ -370,11 +371,12 @@ __device__ __forceinline__ void unpack8_bf16(const uint4& u, float (&v)[8]) {
 // conflicts.  ALT: consecutive rounds stage into different arrays, so a
 // round needs no barrier before its staging (the previous user of its array
 // finished two rounds earlier, before the last round's barrier).
-template <int BM, int BN, int R, bool ALT, typename SF, typename AT, typename AN, typename FT, typename FN>
-__device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[GemmT<BM, BN>::MS][GemmT<BM, BN>::NS],
+template <int BM, int BN, int R, bool ALT, int WCX = 0, typename SF, typename AT, typename AN, typename FT,
+          typename FN>
+__device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[GemmT<BM, BN, WCX>::MS][GemmT<BM, BN, WCX>::NS],
                                                 SF&& stage, bool do_t,
                                                 bool do_n, AT&& aux_t, AN&& aux_n, FT&& out_t, FN&& out_n) {
-  using G = GemmT<BM, BN>;
+  using G = GemmT<BM, BN, WCX>;
   constexpr int HM = BM / 2, QR = BM / (2 * R), RM = BM / R, MR = G::MS / R, SPR = RM + 2;
   static_assert(G::MS % R == 0, "whole blocks per round");
   constexpr int CPR = RM / 8;                 // column-run chunks per staged row
@@ -413,7 +415,7 @@ __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[GemmT<BM, 
       constexpr int sl = q / (G::NS * 4), u = (q / 4) % G::NS, g = q % 4;
       const int s = rd * MR + sl;
       const int il = wr * QR + sl * 32 + 8 * g + 4 * (lane >> 5);
-      float* p = st + blk_col<BM, BN>(u) * SPR + il;
+      float* p = st + blk_col<BM, BN, WCX>(u) * SPR + il;
       *reinterpret_cast<float2*>(p) = make_float2(acc[s][u][4 * g], acc[s][u][4 * g + 1]);
       *reinterpret_cast<float2*>(p + 2) = make_float2(acc[s][u][4 * g + 2], acc[s][u][4 * g + 3]);
     });
@@ -469,11 +471,19 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
 // ---------------------------------------------------------------------------
 // Symmetric products (bf16): kind 0 Gram, kind 1 polynomial.  Square tiles.
 // ---------------------------------------------------------------------------
+// The symmetric products run 256 x 256 tiles on four waves (one per SIMD,
+// each 128 x 128): against eight waves, the 8 x 4096^2 Gram is 3% faster
+// (the combine, which reads one operand through transposing reads, keeps
+// eight).
+template <int BT>
+constexpr int kSyrkWC = BT == 256 ? 2 : 0;
+
 template <int BT, int KIND>
-__global__ __launch_bounds__((GemmT<BT, BT>::NT), 1) void k_syrk_bf16(StepArgs a, const Tile* __restrict__ tiles, int ntiles,
+__global__ __launch_bounds__((GemmT<BT, BT, kSyrkWC<BT>>::NT), 1) void k_syrk_bf16(StepArgs a, const Tile* __restrict__ tiles, int ntiles,
                                                    int src_x, int first, Coeffs cf) {
   constexpr int kind = KIND;
-  using G = GemmT<BT, BT>;
+  constexpr int WCX = kSyrkWC<BT>;
+  using G = GemmT<BT, BT, WCX>;
   __shared__ typename G::Smem sm;
   const Tile t = tiles[xcd_remap(blockIdx.x, ntiles)];
   const MatDesc& d = a.desc[t.mat];
@@ -494,7 +504,7 @@ __global__ __launch_bounds__((GemmT<BT, BT>::NT), 1) void k_syrk_bf16(StepArgs a
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[s][u][r] = 0.0f;
   // A diagonal tile multiplies a panel by itself: it is loaded once.
-  mma_bf16<BT, BT, false>(P + static_cast<int64_t>(t.ti) * BT * ld, ld, P + static_cast<int64_t>(t.tj) * BT * ld, ld,
+  mma_bf16<BT, BT, false, false, WCX>(P + static_cast<int64_t>(t.ti) * BT * ld, ld, P + static_cast<int64_t>(t.tj) * BT * ld, ld,
                           static_cast<int>(ld), sm.buf[0], sm.buf[1], acc, t.ti == t.tj);
 
   const float alpha = (kind == 0) ? (first ? a.scal[d.scal_idx].inv_nu2 : 1.0f) : cf.c;
@@ -532,7 +542,7 @@ __global__ __launch_bounds__((GemmT<BT, BT>::NT), 1) void k_syrk_bf16(StepArgs a
     fin(v, aux, diag_tile ? i - j0 : -1);
     store8(dst, (gi0 + i) * ldo + gj0 + j0, DT_BF16, v);
   };
-  staged_epilogue<BT, BT, 2, false>(acc, [&](int) { return sm.st; }, true, t.ti != t.tj, aux_t, aux_n, out_t, out_n);
+  staged_epilogue<BT, BT, 2, false, WCX>(acc, [&](int) { return sm.st; }, true, t.ti != t.tj, aux_t, aux_n, out_t, out_n);
 }
 
 // ---------------------------------------------------------------------------
@@ -843,7 +853,7 @@ hipError_t launch_syrk(const StepArgs& a, const Tile* tiles, int n, int bt, int 
     return hipGetLastError();
   }
 #define MUON_SYRK(BT, K) \
-  hipLaunchKernelGGL((k_syrk_bf16<BT, K>), dim3(n), dim3(GemmT<BT, BT>::NT), 0, s, a, tiles, n, src_x, f, cf)
+  hipLaunchKernelGGL((k_syrk_bf16<BT, K>), dim3(n), dim3(GemmT<BT, BT, kSyrkWC<BT>>::NT), 0, s, a, tiles, n, src_x, f, cf)
   if (bt == 256) {
     if (kind == 0) MUON_SYRK(256, 0); else MUON_SYRK(256, 1);
   } else if (bt == 128) {
