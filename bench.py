@@ -54,13 +54,13 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 GEMM_SOURCES = ("dimuon_newton_schulz_amd/csrc/gemm_kernels.hip", "dimuon_newton_schulz_amd/csrc/api.hip",
                 "dimuon_newton_schulz_amd/csrc/common.h")
 MEASURED_GEMM = {
-    "sources_sha256": "bfd2736a9b72b5d732cb87968f91afb62cb7999f059e33f1cd3b8ce8fd2d1d76",
-    "gpt2_small_12x4_bf16": {"fetch_kib": [134329.5, 5247.2], "write_kib": [163840.0, 2048.0],
-                             "mfma_busy_frac": 0.362, "clock_ghz": 2.18},
-    "square_8x4096x4096_bf16": {"fetch_kib": [786599.6], "write_kib": [262195.8],
-                                "mfma_busy_frac": 0.571, "clock_ghz": 1.96},
-    "moe_64x(2048x1408+1408x2048)_bf16": {"fetch_kib": [967350.7], "write_kib": [786441.9],
-                                          "mfma_busy_frac": 0.468, "clock_ghz": 2.01},
+    "sources_sha256": "6cce4ea635a5c3a7f929b4fb9d9183dea47165db4199bdaa177576641878d366",
+    "gpt2_small_12x4_bf16": {"fetch_kib": [134258.5, 5242.8], "write_kib": [163840.0, 2048.0],
+                             "mfma_busy_frac": 0.366, "clock_ghz": 2.12},
+    "square_8x4096x4096_bf16": {"fetch_kib": [786598.6], "write_kib": [262202.0],
+                                "mfma_busy_frac": 0.573, "clock_ghz": 1.95},
+    "moe_64x(2048x1408+1408x2048)_bf16": {"fetch_kib": [959216.0], "write_kib": [786444.5],
+                                          "mfma_busy_frac": 0.473, "clock_ghz": 1.95},
 }
 
 
