@@ -12,7 +12,7 @@ import torch
 
 import oracle as O
 
-# Tolerances (north star of the method's step, read as stated):
+# Tolerances (the step's stated accuracy bounds, read as stated):
 #   bf16 NS products: max |O_gpu - O_ref| <= 2e-2 on O itself (o_out: the
 #     step before the learning rate; for Dimuon after the post-scale and the
 #     norm fix), for Muon and Dimuon alike;
