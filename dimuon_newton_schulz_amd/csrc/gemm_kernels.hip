@@ -586,11 +586,16 @@ __global__ __launch_bounds__((GemmT<BM, BN>::NT), 1) void k_combine_bf16(StepArg
   // Dimuon's norm partials: sum of v^2 and of (fr v fc)^2 over the tile, with
   // fr, fc the factors of the Gram orientation's rows and columns (the factor
   // arrays are zero in the padding).
-  auto factors8 = [&](const MUON_GLOBAL float* f, int64_t at, float (&r)[8]) {
-    const float4 lo = *reinterpret_cast<const MUON_GLOBAL float4*>(f + at);
-    const float4 hi = *reinterpret_cast<const MUON_GLOBAL float4*>(f + at + 4);
-    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
-    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+  // The tile's row factors, then its column factors, staged in LDS once
+  // before the epilogue (published by its first barrier) instead of being
+  // fetched in every staging round (rows beyond the Gram side: zero).
+  __shared__ float fac[LAST ? BM + BN : 1];
+  if (LAST && partials)
+    for (int e = threadIdx.x; e < BM + BN; e += G::NT)
+      fac[e] = e < BM ? (gi0 + e < d.KP ? dgr[gi0 + e] : 0.0f) : dgc[gj0 + e - BM];
+  auto factors8 = [&](int at, float (&r)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = fac[at + e];
   };
   auto accum = [&](float fr, float v, float fc) {
     const float p = (fr * v) * fc;
@@ -627,8 +632,8 @@ __global__ __launch_bounds__((GemmT<BM, BN>::NT), 1) void k_combine_bf16(StepArg
     fin(v, aux);
     if (LAST && partials) {
       float fr[8];
-      factors8(dgr, gi0 + i0, fr);
-      const float fc = dgc[gj0 + j];
+      factors8(i0, fr);
+      const float fc = fac[BM + j];
 #pragma unroll
       for (int e = 0; e < 8; ++e) accum(fr[e], v[e], fc);
     }
@@ -639,8 +644,8 @@ __global__ __launch_bounds__((GemmT<BM, BN>::NT), 1) void k_combine_bf16(StepArg
     fin(v, aux);
     if (LAST && partials) {
       float fc[8];
-      factors8(dgc, gj0 + j0, fc);
-      const float fr = dgr[gi0 + i];
+      factors8(BM + j0, fc);
+      const float fr = fac[i];
 #pragma unroll
       for (int e = 0; e < 8; ++e) accum(fr, v[e], fc[e]);
     }
