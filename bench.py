@@ -54,13 +54,13 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 GEMM_SOURCES = ("dimuon_newton_schulz_amd/csrc/gemm_kernels.hip", "dimuon_newton_schulz_amd/csrc/api.hip",
                 "dimuon_newton_schulz_amd/csrc/common.h")
 MEASURED_GEMM = {
-    "sources_sha256": "6cce4ea635a5c3a7f929b4fb9d9183dea47165db4199bdaa177576641878d366",
-    "gpt2_small_12x4_bf16": {"fetch_kib": [134258.5, 5242.8], "write_kib": [163840.0, 2048.0],
-                             "mfma_busy_frac": 0.366, "clock_ghz": 2.12},
-    "square_8x4096x4096_bf16": {"fetch_kib": [786598.6], "write_kib": [262202.0],
-                                "mfma_busy_frac": 0.573, "clock_ghz": 1.95},
-    "moe_64x(2048x1408+1408x2048)_bf16": {"fetch_kib": [959216.0], "write_kib": [786444.5],
-                                          "mfma_busy_frac": 0.473, "clock_ghz": 1.95},
+    "sources_sha256": "3467c3709f08450eb4b729d3d50ff24a74c684aa8a4be7798a7d39652ee69f9f",
+    "gpt2_small_12x4_bf16": {"fetch_kib": [134276.1, 5247.3], "write_kib": [163840.0, 2048.0],
+                             "mfma_busy_frac": 0.365, "clock_ghz": 2.15},
+    "square_8x4096x4096_bf16": {"fetch_kib": [786618.5], "write_kib": [262197.0],
+                                "mfma_busy_frac": 0.572, "clock_ghz": 1.95},
+    "moe_64x(2048x1408+1408x2048)_bf16": {"fetch_kib": [971561.7], "write_kib": [786442.6],
+                                          "mfma_busy_frac": 0.471, "clock_ghz": 1.98},
 }
 
 
