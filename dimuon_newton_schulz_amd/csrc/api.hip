@@ -68,6 +68,9 @@ bool finite(float x) { return std::isfinite(x); }
 struct Plan {
   std::vector<MatDesc> desc;
   std::vector<Tile> k3, k5, cond;
+  // Update tiles of the matrices whose Muon update the last combine does not
+  // apply (a Dimuon step updates every matrix with k5).
+  std::vector<Tile> k5u;
   // GEMM tile lists, one launch each; bm x bn tiles (symmetric products: square)
   struct GemmList { int bm, bn; std::vector<Tile> tiles; size_t off; };
   std::vector<GemmList> syrk, comb;
@@ -83,7 +86,7 @@ struct Plan {
   struct ThinGroup { int kp; std::vector<Tile> tiles; size_t off; };
   std::vector<ThinGroup> thin;
   // byte offsets in the workspace
-  size_t desc_off = 0, scal_off = 0, k3_off = 0, k5_off = 0, cond_off = 0, gen_off = 0;
+  size_t desc_off = 0, scal_off = 0, k3_off = 0, k5_off = 0, k5u_off = 0, cond_off = 0, gen_off = 0;
   size_t table_bytes = 0;   // uploaded prefix of the workspace
   size_t total_bytes = 0;   // whole workspace
   std::vector<unsigned char> table;
@@ -413,8 +416,15 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
       p.gen.push_back(static_cast<uint16_t>(i));
       for (int ti = 0; ti < d.KP / 64; ++ti)
         for (int tj = 0; tj < d.NP / 64; ++tj) p.k3.push_back({static_cast<uint16_t>(i), (uint16_t)ti, (uint16_t)tj, 0});
+      // A Muon step's last bf16 combine applies the update itself where every
+      // row of W is a whole number of 16-byte bf16 runs.
+      d.fuse_upd = (cfg->ns_dtype == MUON_BF16 && cfg->w_dtype == MUON_BF16 && cfg->ns_steps > 0 && d.n % 8 == 0)
+                       ? 1 : 0;
       for (int ti = 0; ti < ceil_div(d.m, 64); ++ti)
-        for (int tj = 0; tj < ceil_div(d.n, 64); ++tj) p.k5.push_back({static_cast<uint16_t>(i), (uint16_t)ti, (uint16_t)tj, 0});
+        for (int tj = 0; tj < ceil_div(d.n, 64); ++tj) {
+          p.k5.push_back({static_cast<uint16_t>(i), (uint16_t)ti, (uint16_t)tj, 0});
+          if (!d.fuse_upd) p.k5u.push_back(p.k5.back());
+        }
       d.ncond = static_cast<int32_t>(ceil_div(d.mpad + d.npad, 256));
       for (int c = 0; c < d.ncond; ++c) p.cond.push_back({static_cast<uint16_t>(i), static_cast<uint16_t>(c), 0, 0});
     }
@@ -437,6 +447,7 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
   for (auto& l : p.comb) l.off = take(sizeof(Tile) * l.tiles.size());
   for (auto& l : p.comb_pad) l.off = take(sizeof(Tile) * l.tiles.size());
   p.k5_off = take(sizeof(Tile) * p.k5.size());
+  p.k5u_off = take(sizeof(Tile) * p.k5u.size());
   p.cond_off = take(sizeof(Tile) * p.cond.size());
   p.gen_off = take(sizeof(uint16_t) * p.gen.size());
   for (auto& g : p.thin) g.off = take(sizeof(Tile) * g.tiles.size());
@@ -483,6 +494,7 @@ muon_status_t build_plan(const muon_matrix_t* mats, int64_t count, const muon_co
     for (auto& l : p.comb) put(p.table, l.off, l.tiles);
     for (auto& l : p.comb_pad) put(p.table, l.off, l.tiles);
     put(p.table, p.k5_off, p.k5);
+    put(p.table, p.k5u_off, p.k5u);
     put(p.table, p.cond_off, p.cond);
     put(p.table, p.gen_off, p.gen);
     for (auto& g : p.thin) put(p.table, g.off, g.tiles);
@@ -705,7 +717,11 @@ muon_status_t launch_all(const Plan& p, const StepArgs& a, const Coeffs* cf, int
                     launch_combine(a, tl(l.off), nt(l), l.bm, l.bn, src, dst, first, last, true, cf[t], s));
     }
     if (dimuon) MUON_LAUNCH(MUON_LAUNCH_POSTNORM, launch_post_finalize(a, il(p.gen_off), ng, s));
-    MUON_LAUNCH(MUON_LAUNCH_UPDATE, launch_update(a, tl(p.k5_off), static_cast<int>(p.k5.size()), s));
+    // Muon: matrices with fuse_upd were updated by the last combine.
+    const std::vector<Tile>& upd = dimuon ? p.k5 : p.k5u;
+    if (!upd.empty())
+      MUON_LAUNCH(MUON_LAUNCH_UPDATE,
+                  launch_update(a, tl(dimuon ? p.k5_off : p.k5u_off), static_cast<int>(upd.size()), s));
   }
   g_hook.last_count = g_hook.next;
   return MUON_OK;

@@ -38,6 +38,7 @@ struct alignas(16) MatDesc {
   int32_t KP, NP;         // padded k, N (general path)
   int32_t tall;           // m > n: the Gram orientation is the transpose
   float update_scale;
+  int32_t fuse_upd;       // Muon: the last combine applies the weight update (bf16 W, n % 8 == 0)
   int64_t x_off[4];       // X (KP x NP) and X^T (NP x KP, fp32 mode only), ping (0,1) and pong (2,3), ns dtype
   int64_t a_off;          // A = X X^T, KP x KP, ns dtype
   int64_t b_off;          // B = bA + c A A, KP x KP, ns dtype

@@ -370,9 +370,12 @@ __device__ __forceinline__ void unpack8_bf16(const uint4& u, float (&v)[8]) {
 // il) and the row-run reads (16 lanes along il x 4 along j) free of bank
 // conflicts.  ALT: consecutive rounds stage into different arrays, so a
 // round needs no barrier before its staging (the previous user of its array
-// finished two rounds earlier, before the last round's barrier).
-template <int BM, int BN, int R, bool ALT, int WCX = 0, typename SF, typename AT, typename AN, typename FT,
-          typename FN>
+// finished two rounds earlier, before the last round's barrier).  AHEAD:
+// each round's operand runs (both kinds) are fetched one round early, the
+// first round's before any staging, so that their latency is hidden behind
+// a round of LDS work (two rounds of operands in registers).
+template <int BM, int BN, int R, bool ALT, int WCX = 0, bool AHEAD = false, typename SF, typename AT, typename AN,
+          typename FT, typename FN>
 __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[GemmT<BM, BN, WCX>::MS][GemmT<BM, BN, WCX>::NS],
                                                 SF&& stage, bool do_t,
                                                 bool do_n, AT&& aux_t, AN&& aux_n, FT&& out_t, FN&& out_n) {
@@ -383,6 +386,7 @@ __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[GemmT<BM, 
   constexpr int CT = BN * CPR / G::NT;        // column-run chunks per thread and round
   constexpr int NB = RM / 16;                 // blocks of 16 staged rows (row runs)
   constexpr int CN = RM * (BN / 8) / G::NT;   // row-run chunks per thread and round
+  constexpr int NSLOT = AHEAD ? 2 : 1;
   static_assert(BN * CPR % G::NT == 0 && RM * (BN / 8) % G::NT == 0, "whole chunks per thread");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wr = wave / G::WC;
   auto t_pos = [&](int q, int& j, int& il) {
@@ -396,18 +400,41 @@ __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[GemmT<BM, 
     il = (r % NB) * 16 + i16;
     j0 = ((r / NB) * 4 + jl) * 8;
   };
+  auto row_in = [&](int rd, int il) { return (il / QR) * HM + rd * QR + il % QR; };
+  decltype(aux_t(0, 0)) xt[NSLOT][CT];
+  decltype(aux_n(0, 0)) xn[NSLOT][CN];
+  auto fetch_t = [&](auto rdc) {
+    constexpr int rd = rdc, sl = rd % NSLOT;
+    static_for<0, CT>([&](auto q) {
+      int j, il;
+      t_pos(q, j, il);
+      xt[sl][q] = aux_t(j, row_in(rd, il));
+    });
+  };
+  auto fetch_n = [&](auto rdc) {
+    constexpr int rd = rdc, sl = rd % NSLOT;
+    static_for<0, CN>([&](auto q) {
+      int il, j0;
+      n_pos(q, il, j0);
+      xn[sl][q] = aux_n(row_in(rd, il), j0);
+    });
+  };
+  if constexpr (AHEAD) {
+    if (do_t) fetch_t(std::integral_constant<int, 0>{});
+    if (do_n) fetch_n(std::integral_constant<int, 0>{});
+  }
   static_for<0, R>([&](auto rdc) {
-    constexpr int rd = rdc;
+    constexpr int rd = rdc, sl = rd % NSLOT;
     float* st = stage(rd);
-    auto row_of = [&](int il) { return (il / QR) * HM + rd * QR + il % QR; };
-    decltype(aux_t(0, 0)) xt[CT];
-    decltype(aux_n(0, 0)) xn[CN];
-    if (do_t)
-      static_for<0, CT>([&](auto q) {
-        int j, il;
-        t_pos(q, j, il);
-        xt[q] = aux_t(j, row_of(il));
-      });
+    auto row_of = [&](int il) { return row_in(rd, il); };
+    if constexpr (AHEAD) {
+      if constexpr (rd + 1 < R) {
+        if (do_t) fetch_t(std::integral_constant<int, rd + 1>{});
+        if (do_n) fetch_n(std::integral_constant<int, rd + 1>{});
+      }
+    } else if (do_t) {
+      fetch_t(rdc);
+    }
     // The main loop's stages, or the round that last used this array, are
     // no longer read.
     if (rd == 0 || !ALT) __syncthreads();
@@ -422,12 +449,7 @@ __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[GemmT<BM, 
     __syncthreads();
     // Row-run operands are fetched now and arrive while the column runs are
     // written.
-    if (do_n)
-      static_for<0, CN>([&](auto q) {
-        int il, j0;
-        n_pos(q, il, j0);
-        xn[q] = aux_n(row_of(il), j0);
-      });
+    if (!AHEAD && do_n) fetch_n(rdc);
     if (do_t)
       static_for<0, CT>([&](auto q) {
         int j, il;
@@ -440,7 +462,7 @@ __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[GemmT<BM, 
           v[e] = w.x;
           v[e + 1] = w.y;
         }
-        out_t(j, row_of(il), v, xt[q]);
+        out_t(j, row_of(il), v, xt[sl][q]);
       });
     if (do_n)
       static_for<0, CN>([&](auto q) {
@@ -449,7 +471,7 @@ __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[GemmT<BM, 
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = st[(j0 + e) * SPR + il];
-        out_n(row_of(il), j0, v, xn[q]);
+        out_n(row_of(il), j0, v, xn[sl][q]);
       });
   });
 }
@@ -582,6 +604,29 @@ __global__ __launch_bounds__((GemmT<BM, BN>::NT), 1) void k_combine_bf16(StepArg
   void* dst_n = last ? (d.tall ? nullptr : a.ws + d.z_off) : a.ws + d.x_off[2 * dst_x];
   void* dst_t = last && d.tall ? a.ws + d.z_off : nullptr;
   constexpr int32_t odt = DT_BF16;
+  // Muon, matrices flagged fuse_upd (bf16 W, rows of whole 8-element runs):
+  // the last combine applies W <- W - lr (s O + wd W) itself, with O the last
+  // iterate rounded to bf16 as Z would be stored, so the result is the one
+  // the separate update pass gives.  Z is then not written.  W's 8-element
+  // runs are fetched ahead of the staging, as operands; the same run in the
+  // caller's layout is a row run for a wide matrix and a column run (down
+  // the Gram side) for a tall one.
+  const bool upd = LAST && !XTERM && !a.dimuon && d.fuse_upd;
+  auto w_idx = [&](int64_t wr, int64_t wc) { return (wr < d.m && wc < d.n) ? wr * d.n + wc : int64_t(-1); };
+  auto update8 = [&](float (&v)[8], const uint4& wq, int64_t at) {
+    if (at < 0) return;
+    float w[8], o[8];
+    unpack8_bf16(wq, w);
+    unpack8_bf16(make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                            pack_bf16x2(v[6], v[7])), o);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float u = __builtin_fmaf(d.update_scale, o[e], a.weight_decay * w[e]);
+      w[e] = __builtin_fmaf(-a.lr, u, w[e]);
+    }
+    store8(d.w, at, DT_BF16, w);
+    if (d.o_out) store8(d.o_out, at, DT_F32, o);
+  };
   float sz = 0.0f, sp = 0.0f;
   // Dimuon's norm partials: sum of v^2 and of (fr v fc)^2 over the tile, with
   // fr, fc the factors of the Gram orientation's rows and columns (the factor
@@ -611,11 +656,17 @@ __global__ __launch_bounds__((GemmT<BM, BN>::NT), 1) void k_combine_bf16(StepArg
       for (int e = 0; e < 8; ++e) h[e] = gmem(X)[(gi0 + i0 + e) * d.NP + gj0 + j];
       return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
     } else {
-      return make_uint4(0, 0, 0, 0);
+      const int64_t at = upd ? w_idx(gj0 + j, gi0 + i0) : int64_t(-1);
+      return at >= 0 ? fetch8_bf16(static_cast<const uint16_t*>(d.w), at) : make_uint4(0, 0, 0, 0);
     }
   };
   auto aux_n = [&](int i, int j0) {
-    return XTERM ? fetch8_bf16(X, (gi0 + i) * d.NP + gj0 + j0) : make_uint4(0, 0, 0, 0);
+    if constexpr (XTERM) {
+      return fetch8_bf16(X, (gi0 + i) * d.NP + gj0 + j0);
+    } else {
+      const int64_t at = upd ? w_idx(gi0 + i, gj0 + j0) : int64_t(-1);
+      return at >= 0 ? fetch8_bf16(static_cast<const uint16_t*>(d.w), at) : make_uint4(0, 0, 0, 0);
+    }
   };
   auto fin = [&](float (&v)[8], const uint4& aux) {
     float x[8];
@@ -637,7 +688,8 @@ __global__ __launch_bounds__((GemmT<BM, BN>::NT), 1) void k_combine_bf16(StepArg
 #pragma unroll
       for (int e = 0; e < 8; ++e) accum(fr[e], v[e], fc);
     }
-    store8(dst_t, (gj0 + j) * d.KP + gi0 + i0, odt, v);
+    if (upd) update8(v, aux, w_idx(gj0 + j, gi0 + i0));
+    else store8(dst_t, (gj0 + j) * d.KP + gi0 + i0, odt, v);
   };
   auto out_n = [&](int i, int j0, float (&v)[8], const uint4& aux) {
     if (LAST && gi0 + i >= d.KP) return;
@@ -649,10 +701,20 @@ __global__ __launch_bounds__((GemmT<BM, BN>::NT), 1) void k_combine_bf16(StepArg
 #pragma unroll
       for (int e = 0; e < 8; ++e) accum(fr, v[e], fc[e]);
     }
-    store8(dst_n, (gi0 + i) * d.NP + gj0 + j0, odt, v);
+    if (upd) update8(v, aux, w_idx(gi0 + i, gj0 + j0));
+    else store8(dst_n, (gi0 + i) * d.NP + gj0 + j0, odt, v);
   };
   auto stage = [&](int rd) { return reinterpret_cast<float*>(rd & 1 ? ring1 : ring0); };
-  staged_epilogue<BM, BN, C::R, true>(acc, stage, dst_t != nullptr, dst_n != nullptr, aux_t, aux_n, out_t, out_n);
+  if constexpr (LAST) {
+    // One of the two kinds of runs; operands (W, or X for XTERM) fetched a
+    // round ahead.
+    if (dst_t)
+      staged_epilogue<BM, BN, C::R, true, 0, true>(acc, stage, true, false, aux_t, aux_n, out_t, out_n);
+    else
+      staged_epilogue<BM, BN, C::R, true, 0, true>(acc, stage, false, true, aux_t, aux_n, out_t, out_n);
+  } else {
+    staged_epilogue<BM, BN, C::R, true>(acc, stage, dst_t != nullptr, dst_n != nullptr, aux_t, aux_n, out_t, out_n);
+  }
   if (LAST && partials) {
     // The staging arrays are free once every wave has left the epilogue.
     __syncthreads();

@@ -169,6 +169,30 @@ def test_muon_streaming_passes_fused(wdt):
     run_case(wl, "muon", cfg_of(wl, nesterov=True, weight_decay=0.1), scales=[0.5, 2.0, 1.0, 1.5, 0.25])
 
 
+def test_muon_update_in_last_combine():
+    # Muon with bf16 weights: for a matrix whose rows are whole 8-element
+    # runs, the last combine applies the update (O rounded to bf16 as the last
+    # iterate is stored), and the update pass runs only for the others.  Wide
+    # and tall, rows beyond the Gram side's padding, a ragged long side, with
+    # and without weight decay and per-matrix scales, against the oracle.
+    # (The first-step identity test checks it bit for bit against Dimuon,
+    # which always takes the update pass.)
+    shapes = [(384, 1024), (1024, 384), (300, 696), (700, 296), (129, 136)]
+    wl = W.random_batch(shapes, dtype="bf16", ns_dtype="bf16", seed=21)
+    cfg = cfg_of(wl)
+    params = [D.Param(w=m.w.cuda().clone(), g=m.g.cuda().clone(), mom=m.m_prev.cuda().clone()) for m in wl.mats]
+    announce("update in the last combine: launch kinds")
+    assert "update" not in launch_kinds(lambda: D.muon_step(params, cfg))
+    assert launch_kinds(lambda: D.dimuon_step(params, cfg)).count("update") == 1
+    mixed = params + [D.Param(w=params[0].w[:, :999].contiguous(), g=params[0].g[:, :999].contiguous(),
+                              mom=params[0].mom[:, :999].contiguous())]
+    assert launch_kinds(lambda: D.muon_step(mixed, cfg)).count("update") == 1
+    assert launch_kinds(lambda: D.muon_step(params, cfg_of(wl, ns_dtype="f32"))).count("update") == 1
+    del params, mixed
+    run_case(wl, "muon", cfg)
+    run_case(wl, "muon", cfg_of(wl, nesterov=True, weight_decay=0.1), scales=[0.5, 2.0, 1.0, 1.5, 0.25])
+
+
 @pytest.mark.parametrize("variant", ["muon", "dimuon"])
 def test_general_f32_storage(variant):
     shapes = [(200, 333), (333, 200), (64, 1024)]
@@ -324,7 +348,8 @@ def test_moe_scaled_zero_rows():
 # Method properties on the GPU
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("shapes", [[(8, 4096), (4096, 8), (4, 16)], [(300, 700), (700, 300), (256, 256)]])
+@pytest.mark.parametrize("shapes", [[(8, 4096), (4096, 8), (4, 16)], [(300, 700), (700, 300), (256, 256)],
+                                    [(384, 1024), (1024, 384), (300, 696), (700, 296)]])
 def test_first_step_dimuon_equals_muon_bitwise(shapes):
     wl = W.random_batch(shapes, dtype="bf16", ns_dtype="bf16", seed=8, zero_prev=True)
     cfg = cfg_of(wl)
