@@ -37,9 +37,9 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 # profiles/k_thin_lora_batch_64x8x4096.md.
 THIN_SOURCES = ("dimuon_newton_schulz_amd/csrc/thin_kernel.hip", "dimuon_newton_schulz_amd/csrc/common.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "30c10725495475707d8e4c4a3f60c6abed661f71f1647953cb3809472d662332",
-    "k_thin_a": {"fetch_kib": 18158.2, "write_kib": 19012.7},
-    "k_thin_b": {"fetch_kib": 20425.0, "write_kib": 18496.0},
+    "sources_sha256": "963df4ed03f6ab9e3a50a75e63f078ecf1b8a4a7e0eedf695dd12c7844a8b934",
+    "k_thin_a": {"fetch_kib": 18130.1, "write_kib": 19012.9},
+    "k_thin_b": {"fetch_kib": 20388.1, "write_kib": 18496.0},
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
@@ -54,13 +54,13 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 GEMM_SOURCES = ("dimuon_newton_schulz_amd/csrc/gemm_kernels.hip", "dimuon_newton_schulz_amd/csrc/api.hip",
                 "dimuon_newton_schulz_amd/csrc/common.h")
 MEASURED_GEMM = {
-    "sources_sha256": "3467c3709f08450eb4b729d3d50ff24a74c684aa8a4be7798a7d39652ee69f9f",
-    "gpt2_small_12x4_bf16": {"fetch_kib": [134276.1, 5247.3], "write_kib": [163840.0, 2048.0],
-                             "mfma_busy_frac": 0.365, "clock_ghz": 2.15},
-    "square_8x4096x4096_bf16": {"fetch_kib": [786618.5], "write_kib": [262197.0],
-                                "mfma_busy_frac": 0.572, "clock_ghz": 1.95},
-    "moe_64x(2048x1408+1408x2048)_bf16": {"fetch_kib": [971561.7], "write_kib": [786442.6],
-                                          "mfma_busy_frac": 0.471, "clock_ghz": 1.98},
+    "sources_sha256": "944fb14e99f762949713887af1b24717726d3fb4a3d374a8ebb0b45702b66354",
+    "gpt2_small_12x4_bf16": {"fetch_kib": [134383.8, 5244.8], "write_kib": [163840.0, 2048.0],
+                             "mfma_busy_frac": 0.362, "clock_ghz": 2.21},
+    "square_8x4096x4096_bf16": {"fetch_kib": [786674.1], "write_kib": [262196.3],
+                                "mfma_busy_frac": 0.573, "clock_ghz": 1.90},
+    "moe_64x(2048x1408+1408x2048)_bf16": {"fetch_kib": [972927.2], "write_kib": [786448.6],
+                                          "mfma_busy_frac": 0.475, "clock_ghz": 1.89},
 }
 
 
