@@ -189,9 +189,11 @@ typedef enum muon_launch_kind {
   MUON_LAUNCH_NORM = 4,       /* Frobenius norm of the prescaled copy */
   MUON_LAUNCH_GRAM = 5,       /* A = X X^T */
   MUON_LAUNCH_POLY = 6,       /* B = b A + c A A */
-  MUON_LAUNCH_COMBINE = 7,    /* X = a X + B X */
+  MUON_LAUNCH_COMBINE = 7,    /* X = a X + B X (Muon, bf16 weights with rows of whole 8-element
+                                 runs: the last one also applies the weight update) */
   MUON_LAUNCH_POSTNORM = 8,   /* Dimuon norm fix */
-  MUON_LAUNCH_UPDATE = 9,     /* O and the weight update */
+  MUON_LAUNCH_UPDATE = 9,     /* O and the weight update (not emitted when the last combine
+                                 updated every matrix) */
   MUON_LAUNCH_THIN_ENERGY = 10, /* thin path: energies of M_{t-1} (no cached energies) */
   MUON_LAUNCH_THIN_A = 11,    /* thin path pass A: momentum, Gram partials */
   MUON_LAUNCH_MOMENTUM_PRESCALE = 12, /* momentum, Dimuon energies of M_t, conditioned and
