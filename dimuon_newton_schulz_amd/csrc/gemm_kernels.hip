@@ -571,7 +571,7 @@ __global__ __launch_bounds__((GemmT<BT, BT, kSyrkWC<BT>>::NT), 1) void k_syrk_bf
 // Combine (bf16 operands): X' = alpha B X, with B = a I + b A + c A A.
 // XTERM (no iterations: Z = alpha a X): the product is skipped and X read.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, bool LAST, bool XTERM>
+template <int BM, int BN, bool LAST, bool XTERM, bool UPD = false>
 __global__ __launch_bounds__((GemmT<BM, BN>::NT), 1) void k_combine_bf16(StepArgs a, const Tile* __restrict__ tiles, int ntiles,
                                                       int src_x, int dst_x, int first, Coeffs cf) {
   constexpr bool last = LAST;
@@ -604,14 +604,15 @@ __global__ __launch_bounds__((GemmT<BM, BN>::NT), 1) void k_combine_bf16(StepArg
   void* dst_n = last ? (d.tall ? nullptr : a.ws + d.z_off) : a.ws + d.x_off[2 * dst_x];
   void* dst_t = last && d.tall ? a.ws + d.z_off : nullptr;
   constexpr int32_t odt = DT_BF16;
-  // Muon, matrices flagged fuse_upd (bf16 W, rows of whole 8-element runs):
-  // the last combine applies W <- W - lr (s O + wd W) itself, with O the last
+  // Muon (the UPD variant of the last combine), matrices flagged fuse_upd
+  // (bf16 W, rows of whole 8-element runs): it applies W <- W - lr (s O + wd W) itself, with O the last
   // iterate rounded to bf16 as Z would be stored, so the result is the one
   // the separate update pass gives.  Z is then not written.  W's 8-element
   // runs are fetched ahead of the staging, as operands; the same run in the
   // caller's layout is a row run for a wide matrix and a column run (down
   // the Gram side) for a tall one.
-  const bool upd = LAST && !XTERM && !a.dimuon && d.fuse_upd;
+  static_assert(!UPD || (LAST && !XTERM), "the update rides on the last product");
+  const bool upd = UPD && d.fuse_upd;
   auto w_idx = [&](int64_t wr, int64_t wc) { return (wr < d.m && wc < d.n) ? wr * d.n + wc : int64_t(-1); };
   auto update8 = [&](float (&v)[8], const uint4& wq, int64_t at) {
     if (at < 0) return;
@@ -705,7 +706,7 @@ __global__ __launch_bounds__((GemmT<BM, BN>::NT), 1) void k_combine_bf16(StepArg
     else store8(dst_n, (gi0 + i) * d.NP + gj0 + j0, odt, v);
   };
   auto stage = [&](int rd) { return reinterpret_cast<float*>(rd & 1 ? ring1 : ring0); };
-  if constexpr (LAST) {
+  if constexpr (UPD || XTERM) {
     // One of the two kinds of runs; operands (W, or X for XTERM) fetched a
     // round ahead.
     if (dst_t)
@@ -949,6 +950,9 @@ hipError_t launch_combine(const StepArgs& a, const Tile* tiles, int n, int bm, i
     if (!last) return hipErrorInvalidValue;                                                                  \
     hipLaunchKernelGGL((k_combine_bf16<BM, BN, true, true>), dim3(n), dim3(GemmT<BM, BN>::NT), 0, s, a, tiles, n, src_x,   \
                        dst_x, f, cf);                                                                        \
+  } else if (last && !a.dimuon) {                                                                            \
+    hipLaunchKernelGGL((k_combine_bf16<BM, BN, true, false, true>), dim3(n), dim3(GemmT<BM, BN>::NT), 0, s, a, tiles, n, \
+                       src_x, dst_x, f, cf);                                                                 \
   } else if (last) {                                                                                         \
     hipLaunchKernelGGL((k_combine_bf16<BM, BN, true, false>), dim3(n), dim3(GemmT<BM, BN>::NT), 0, s, a, tiles, n, src_x,  \
                        dst_x, f, cf);                                                                        \
