@@ -54,13 +54,13 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 GEMM_SOURCES = ("dimuon_newton_schulz_amd/csrc/gemm_kernels.hip", "dimuon_newton_schulz_amd/csrc/api.hip",
                 "dimuon_newton_schulz_amd/csrc/common.h")
 MEASURED_GEMM = {
-    "sources_sha256": "b8f81596fb90e4d474120e79988f5d7c64a70d15569aa0ffe1d94bd0b78a0764",
-    "gpt2_small_12x4_bf16": {"fetch_kib": [134278.2, 5247.3], "write_kib": [163840.0, 2048.0],
-                             "mfma_busy_frac": 0.364, "clock_ghz": 2.16},
-    "square_8x4096x4096_bf16": {"fetch_kib": [786598.0], "write_kib": [262212.2],
-                                "mfma_busy_frac": 0.574, "clock_ghz": 1.95},
-    "moe_64x(2048x1408+1408x2048)_bf16": {"fetch_kib": [957247.2], "write_kib": [786446.2],
-                                          "mfma_busy_frac": 0.472, "clock_ghz": 1.97},
+    "sources_sha256": "c1fe7c74e5f02ba6840d26a340c63cfc61d80f4cdd7578bd6e82ed55e761253a",
+    "gpt2_small_12x4_bf16": {"fetch_kib": [134318.0, 5247.3], "write_kib": [163840.0, 2048.0],
+                             "mfma_busy_frac": 0.363, "clock_ghz": 2.18},
+    "square_8x4096x4096_bf16": {"fetch_kib": [786603.3], "write_kib": [262203.5],
+                                "mfma_busy_frac": 0.574, "clock_ghz": 1.96},
+    "moe_64x(2048x1408+1408x2048)_bf16": {"fetch_kib": [963561.3], "write_kib": [786441.1],
+                                          "mfma_busy_frac": 0.471, "clock_ghz": 1.95},
 }
 
 

@@ -166,14 +166,23 @@ __device__ __forceinline__ void issue_stage(const MUON_GLOBAL uint16_t* P, int64
 // i mod 4 of the 8-byte reads of lanes 4 e + i / 4, e = 0..3, so lane m of the
 // group reads the four n-values 4 (m mod 4) .. + 3 of its 16-column half at
 // k-row 8 (l / 32) + m / 4, and four k-rows further down for the second read.
-template <int BM, int BN, bool QT, bool F32 = false, int WCX = 0>
+//
+// NB = 4 (a deep ring, for 128 x 128 lists of at most one workgroup per CU,
+// where the LDS of a second workgroup is free): four buffers b0 .. b3,
+// stages 0 .. 3 issued up front, and stage kt+3 issued into stage kt-1's
+// buffer as stage kt starts, so up to three stages are in flight while one
+// is multiplied.  The MFMAs and their k order are those of the two-buffer
+// loop, so the results are the same bit for bit.
+template <int BM, int BN, bool QT, bool F32 = false, int WCX = 0, int NB = 2>
 __device__ __forceinline__ void mma_bf16(const uint16_t* Pg, int64_t ldp, const uint16_t* Qg, int64_t ldq, int K,
                                          uint16_t* b0, uint16_t* b1,
                                          f32x16_t (&acc)[GemmT<BM, BN, WCX>::MS][GemmT<BM, BN, WCX>::NS],
-                                         bool same = false) {
+                                         bool same = false, uint16_t* b2 = nullptr, uint16_t* b3 = nullptr) {
   using G = GemmT<BM, BN, WCX>;
   constexpr int MS = G::MS, NS = G::NS, LPS = G::LPS, WN = BN / G::WC;
   static_assert(NQ % 2 == 0, "fragment sets alternate");
+  static_assert(NB == 2 || NB == 4, "two or four ring buffers");
+  static_assert(NB == 2 || 3 * LPS <= 63, "vector-memory counter range");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = wave / G::WC, wc = wave % G::WC;
   const MUON_GLOBAL uint16_t* P = gmem(Pg);
@@ -181,9 +190,16 @@ __device__ __forceinline__ void mma_bf16(const uint16_t* Pg, int64_t ldp, const 
   const int nk = K / LBK;
   // Every wave's stage-0 loads are issued before any stage-1 load (the
   // barrier waits for issue, not for data): the first stage arrives first.
+  // (The deep ring loads both panels of a diagonal tile too, so that every
+  // stage is the same number of loads.)
+  if constexpr (NB == 4) same = false;
   issue_stage<BM, BN, QT, 0, G::LPS, WCX>(P, ldp, Q, ldq, 0, b0, same);
   __builtin_amdgcn_s_barrier();
   issue_stage<BM, BN, QT, 0, G::LPS, WCX>(P, ldp, Q, ldq, 1, b1, same);
+  if constexpr (NB == 4) {
+    issue_stage<BM, BN, QT, 0, G::LPS, WCX>(P, ldp, Q, ldq, min(2, nk - 1), b2);
+    issue_stage<BM, BN, QT, 0, G::LPS, WCX>(P, ldp, Q, ldq, min(3, nk - 1), b3);
+  }
   // Fragment addresses (elements within a stage): row (lane & 31) of each
   // 32-row block, logical chunk 2 q + (lane >> 5) for k-step q.  The swizzle
   // of a row depends on its index mod 16 only, i.e. on lane & 31.
@@ -287,25 +303,83 @@ __device__ __forceinline__ void mma_bf16(const uint16_t* Pg, int64_t ldp, const 
     }
     sync();
   };
-  // Stage 0 landed (stage 1's loads were issued after it).
-  if (same) wait_vm<G::LA>();
-  else wait_vm<LPS>();
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  read_step(b0, 0, fa[0], fb[0]);
+  if constexpr (NB == 4) {
+    // Every step issues one stage's loads (past the last stage, the last
+    // stage again into a buffer that is no longer read), so that each wait
+    // is a fixed count: the compiler then keeps the loads of later stages in
+    // flight across the reads of the current one.
+    // After stage kt: this wave's reads of it are complete and stage kt+1
+    // has landed (the two stages issued after it may still be in flight).
+    auto sync_deep = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      wait_vm<2 * LPS>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // Stage kt from cur; stage kt+3 into ib (stage kt-1's buffer, which no
+    // wave reads any more), half of it before the first MFMAs.
+    auto deep_step = [&](uint16_t* cur, uint16_t* ib, int kt) {
+      const int st = min(kt + 3, nk - 1);
+      read_step(cur, 0, fa[0], fb[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_stage<BM, BN, QT, 0, LPS / 2, WCX>(P, ldp, Q, ldq, st, ib);
+      mfma_step(fa[(NQ - 1) & 1], fb[(NQ - 1) & 1]);
+      issue_stage<BM, BN, QT, LPS / 2, LPS, WCX>(P, ldp, Q, ldq, st, ib);
 #pragma unroll
-  for (int q = 1; q < NQ; ++q) {
-    read_step(b0, q, fa[q & 1], fb[q & 1]);
-    mfma_step(fa[(q - 1) & 1], fb[(q - 1) & 1]);
+      for (int q = 1; q < NQ; ++q) {
+        read_step(cur, q, fa[q & 1], fb[q & 1]);
+        mfma_step(fa[(q - 1) & 1], fb[(q - 1) & 1]);
+      }
+      sync_deep();
+    };
+    wait_vm<3 * LPS>();   // stage 0 landed
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    read_step(b0, 0, fa[0], fb[0]);
+#pragma unroll
+    for (int q = 1; q < NQ; ++q) {
+      read_step(b0, q, fa[q & 1], fb[q & 1]);
+      mfma_step(fa[(q - 1) & 1], fb[(q - 1) & 1]);
+    }
+    sync_deep();
+    // Stage kt lives in buffer kt mod 4 (unrolled by four, so that every
+    // access names its buffer).
+    for (int kt = 1; kt < nk; kt += 4) {
+      deep_step(b1, b0, kt);
+      if (kt + 1 >= nk) break;
+      deep_step(b2, b1, kt + 1);
+      if (kt + 2 >= nk) break;
+      deep_step(b3, b2, kt + 2);
+      if (kt + 3 >= nk) break;
+      deep_step(b0, b3, kt + 3);
+    }
+    mfma_step(fa[(NQ - 1) & 1], fb[(NQ - 1) & 1]);
+    // No load may still be writing the ring when the epilogue reuses it.
+    wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+  } else {
+    // Stage 0 landed (stage 1's loads were issued after it).
+    if (same) wait_vm<G::LA>();
+    else wait_vm<LPS>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    read_step(b0, 0, fa[0], fb[0]);
+#pragma unroll
+    for (int q = 1; q < NQ; ++q) {
+      read_step(b0, q, fa[q & 1], fb[q & 1]);
+      mfma_step(fa[(q - 1) & 1], fb[(q - 1) & 1]);
+    }
+    sync();
+    int kt = 0;
+    for (; kt + 2 < nk; kt += 2) {
+      half_step(b0, b1, kt);
+      half_step(b1, b0, kt + 1);
+    }
+    half_step(b0, b1, kt);   // stage nk-1 (nk is even)
+    mfma_step(fa[(NQ - 1) & 1], fb[(NQ - 1) & 1]);
   }
-  sync();
-  int kt = 0;
-  for (; kt + 2 < nk; kt += 2) {
-    half_step(b0, b1, kt);
-    half_step(b1, b0, kt + 1);
-  }
-  half_step(b0, b1, kt);   // stage nk-1 (nk is even)
-  mfma_step(fa[(NQ - 1) & 1], fb[(NQ - 1) & 1]);
 }
 
 // Calls f(integral_constant<int, I>) for I = I0 .. N-1: compile-time block
@@ -500,13 +574,19 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
 template <int BT>
 constexpr int kSyrkWC = BT == 256 ? 2 : 0;
 
-template <int BT, int KIND>
+// NB = 4: the deep ring (lists of at most one workgroup per CU).
+template <int BT, int KIND, int NB = 2>
 __global__ __launch_bounds__((GemmT<BT, BT, kSyrkWC<BT>>::NT), 1) void k_syrk_bf16(StepArgs a, const Tile* __restrict__ tiles, int ntiles,
                                                    int src_x, int first, Coeffs cf) {
   constexpr int kind = KIND;
   constexpr int WCX = kSyrkWC<BT>;
   using G = GemmT<BT, BT, WCX>;
-  __shared__ typename G::Smem sm;
+  union SmemNB {
+    uint16_t buf[NB][G::STAGE];
+    float st[BT * G::SP];
+  };
+  static_assert(NB == 2 || (BT == 128 && sizeof(SmemNB) <= 163840), "deep ring: 128 x 128 tiles, one per CU");
+  __shared__ typename std::conditional<NB == 2, typename G::Smem, SmemNB>::type sm;
   const Tile t = tiles[xcd_remap(blockIdx.x, ntiles)];
   const MatDesc& d = a.desc[t.mat];
   const uint16_t* P;
@@ -526,8 +606,13 @@ __global__ __launch_bounds__((GemmT<BT, BT, kSyrkWC<BT>>::NT), 1) void k_syrk_bf
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[s][u][r] = 0.0f;
   // A diagonal tile multiplies a panel by itself: it is loaded once.
-  mma_bf16<BT, BT, false, false, WCX>(P + static_cast<int64_t>(t.ti) * BT * ld, ld, P + static_cast<int64_t>(t.tj) * BT * ld, ld,
-                          static_cast<int>(ld), sm.buf[0], sm.buf[1], acc, t.ti == t.tj);
+  if constexpr (NB == 4)
+    mma_bf16<BT, BT, false, false, WCX, 4>(P + static_cast<int64_t>(t.ti) * BT * ld, ld, P + static_cast<int64_t>(t.tj) * BT * ld,
+                                           ld, static_cast<int>(ld), sm.buf[0], sm.buf[1], acc, t.ti == t.tj, sm.buf[2],
+                                           sm.buf[3]);
+  else
+    mma_bf16<BT, BT, false, false, WCX>(P + static_cast<int64_t>(t.ti) * BT * ld, ld, P + static_cast<int64_t>(t.tj) * BT * ld, ld,
+                            static_cast<int>(ld), sm.buf[0], sm.buf[1], acc, t.ti == t.tj);
 
   const float alpha = (kind == 0) ? (first ? a.scal[d.scal_idx].inv_nu2 : 1.0f) : cf.c;
   const uint16_t* E = reinterpret_cast<const uint16_t*>(a.ws + d.a_off);
@@ -907,7 +992,14 @@ __global__ __launch_bounds__((GemmT<FT, FT>::NT), 1) void k_combine_f32(StepArgs
 
 // ---------------------------------------------------------------------------
 // Launchers.  bt / bm, bn: tile sides of the list (128 or 256; fp32 always 128).
+// A bf16 128 x 128 symmetric-product list with no more tiles than the GPU
+// has CUs (a partial round split off a big-tile list, or a small batch) runs
+// one workgroup per CU anyway, so it takes the deep ring: on the 8 x 4096^2
+// set those launches went from 47.6 to about 41.6 us (Gram and polynomial
+// about 1% faster per step, bit-identical results).  The combine's tail
+// lists measured no faster with it and keep the two-buffer ring.
 // ---------------------------------------------------------------------------
+constexpr int kDeepMaxTiles = 256;
 hipError_t launch_syrk(const StepArgs& a, const Tile* tiles, int n, int bt, int kind, int src_x, bool first,
                        Coeffs cf, hipStream_t s) {
   if (n <= 0) return hipSuccess;
@@ -920,10 +1012,13 @@ hipError_t launch_syrk(const StepArgs& a, const Tile* tiles, int n, int bt, int 
       hipLaunchKernelGGL(k_syrk_f32<1>, dim3(n), dim3(GemmT<FT, FT>::NT), 0, s, a, tiles, n, src_x, f, cf);
     return hipGetLastError();
   }
-#define MUON_SYRK(BT, K) \
-  hipLaunchKernelGGL((k_syrk_bf16<BT, K>), dim3(n), dim3(GemmT<BT, BT, kSyrkWC<BT>>::NT), 0, s, a, tiles, n, src_x, f, cf)
+#define MUON_SYRK(BT, K, ...) \
+  hipLaunchKernelGGL((k_syrk_bf16<BT, K, ##__VA_ARGS__>), dim3(n), dim3(GemmT<BT, BT, kSyrkWC<BT>>::NT), 0, s, a, tiles, n, \
+                     src_x, f, cf)
   if (bt == 256) {
     if (kind == 0) MUON_SYRK(256, 0); else MUON_SYRK(256, 1);
+  } else if (bt == 128 && n <= kDeepMaxTiles) {
+    if (kind == 0) MUON_SYRK(128, 0, 4); else MUON_SYRK(128, 1, 4);
   } else if (bt == 128) {
     if (kind == 0) MUON_SYRK(128, 0); else MUON_SYRK(128, 1);
   } else {
