@@ -445,6 +445,29 @@ def test_round_interleave_bit_identical(variant):
 
 
 @pytest.mark.parametrize("variant", ["muon", "dimuon"])
+def test_symmetric_ring_depths_bit_identical(variant):
+    # 8 x 1024^2: the symmetric products run 128 x 128 tiles, 36 per matrix.
+    # The batch's 288 tiles exceed one per CU and take the two-buffer ring; a
+    # matrix alone (36 tiles) takes the four-buffer ring.  The two rings run
+    # the same MFMAs in the same k order: bit for bit.
+    shapes = [(1024, 1024)] * 8
+    wl = W.random_batch(shapes, dtype="bf16", ns_dtype="bf16", seed=43, variant=variant)
+    cfg = cfg_of(wl)
+    fn = D.dimuon_step if variant == "dimuon" else D.muon_step
+    announce(f"ring depths {variant}")
+    together = _batch_params(wl, range(wl.count))
+    fn(together, cfg)
+    for i in (0, 5):
+        alone = _batch_params(wl, [i])
+        fn(alone, cfg)
+        torch.cuda.synchronize()
+        for name in ("w", "mom", "o_out"):
+            np.testing.assert_array_equal(getattr(alone[0], name).float().cpu().numpy(),
+                                          getattr(together[i], name).float().cpu().numpy(),
+                                          err_msg=f"matrix {i} {name}")
+
+
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
 def test_nonfinite_gradient_stays_in_its_matrix(variant):
     # NaN propagates as IEEE arithmetic does (no status word): a NaN in one
     # element of a gradient gives a NaN in that element of M_t and a
