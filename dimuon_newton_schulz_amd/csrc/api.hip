@@ -184,7 +184,8 @@ size_t put(std::vector<unsigned char>& buf, size_t off, const std::vector<T>& v)
 
 // GEMM tiles of the general path.  A 256-wide tile side is possible where
 // the padded side is a multiple of 256; those kernels run one workgroup per
-// CU, the 128 x 128 kernel two.  For each product kind the batch takes the
+// CU, the 128 x 128 symmetric products two (the 128 x 128 combine one).  For
+// each product kind the batch takes the
 // big tiles where they fit, unless the estimated time with 128 x 128 tiles
 // everywhere is lower (few big tiles leave CUs idle in the last round).
 // Within a matrix, tiles are listed in groups of tile rows, column by
@@ -269,11 +270,15 @@ void interleave_rounds(const Plan& p, Plan::GemmList& l) {
 
 void plan_gemm_tiles(Plan& p, bool bf16) {
   auto side = [&](int32_t x, bool big) { return (big && x % 256 == 0) ? 256 : 128; };
-  auto rounds_time = [&](const std::map<std::pair<int, int>, int64_t>& n) {
+  // small_per_cu: 128 x 128 workgroups per CU (two for the symmetric
+  // products; one for the combine, whose 128 x 128 kernel holds a four-buffer
+  // ring).
+  auto rounds_time = [&](const std::map<std::pair<int, int>, int64_t>& n, int small_per_cu) {
     double t = 0.0;
     for (const auto& kv : n) {
       const int bm = kv.first.first, bn = kv.first.second;
-      if (bm == 128 && bn == 128) t += std::ceil(kv.second / (2.0 * kCUs)) * 2.0 / kSmallTileEff;
+      if (bm == 128 && bn == 128)
+        t += std::ceil(kv.second / double(small_per_cu * kCUs)) * small_per_cu / kSmallTileEff;
       else t += std::ceil(kv.second / double(kCUs)) * (bm * bn / 16384.0);
     }
     return t;
@@ -290,7 +295,8 @@ void plan_gemm_tiles(Plan& p, bool bf16) {
         const int64_t rs = d.KP / 128, cs = (kind == 0 ? d.KP : d.NP) / 128;
         ns[{128, 128}] += kind == 0 ? rs * (rs + 1) / 2 : rs * cs;
       }
-      big = rounds_time(nb) < rounds_time(ns);
+      const int per_cu = kind == 0 ? 2 : 1;
+      big = rounds_time(nb, per_cu) < rounds_time(ns, per_cu);
     }
     auto& lists = kind == 0 ? p.syrk : p.comb;
     std::map<std::pair<int, int>, size_t> at;
@@ -311,17 +317,18 @@ void plan_gemm_tiles(Plan& p, bool bf16) {
         d.n_pz = (d.KP / 128) * (d.NP / 128);
       }
     }
-    // A last round of big tiles that fills at most half the CUs goes to the
-    // 128 x 128 list instead (two workgroups per CU): each big tile becomes
-    // its 128 x 128 sub-tiles (for a symmetric product only those on or
-    // above the diagonal).
+    // A last round of big tiles that fills at most half the CUs (a quarter
+    // for the combine, whose 128 x 128 tiles run one per CU) goes to the
+    // 128 x 128 list instead: each big tile becomes its 128 x 128 sub-tiles
+    // (for a symmetric product only those on or above the diagonal).
     if (big) {
       const std::vector<std::pair<int, int>> bigs = {{256, 256}, {128, 256}, {256, 128}};
       for (const auto& key : bigs) {
         const auto bi = at.find(key);
         if (bi == at.end()) continue;
         const size_t n = lists[bi->second].tiles.size(), r = n % kCUs;
-        if (n <= static_cast<size_t>(kCUs) || r == 0 || r > static_cast<size_t>(kCUs / 2)) continue;
+        if (n <= static_cast<size_t>(kCUs) || r == 0 || r > static_cast<size_t>(kind == 0 ? kCUs / 2 : kCUs / 4))
+          continue;
         auto si = at.find({128, 128});
         if (si == at.end()) {
           si = at.emplace(std::make_pair(128, 128), lists.size()).first;

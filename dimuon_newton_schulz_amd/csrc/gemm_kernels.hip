@@ -656,14 +656,28 @@ __global__ __launch_bounds__((GemmT<BT, BT, kSyrkWC<BT>>::NT), 1) void k_syrk_bf
 // Combine (bf16 operands): X' = alpha B X, with B = a I + b A + c A A.
 // XTERM (no iterations: Z = alpha a X): the product is skipped and X read.
 // ---------------------------------------------------------------------------
+//
+// 128 x 128 tiles run the four-buffer ring (four separate arrays, so that
+// the compiler can tell the stages apart), which also makes them run one
+// workgroup per CU.  Two workgroups of the two-buffer 128 x 128 combine on
+// one CU gave results that differed between identical runs (about a
+// thousand elements of X' per launch of 512 tiles, 8 x 1024^2, while its
+// inputs were the same bit for bit); with one workgroup per CU, or with the
+// four-buffer ring, repeated runs agree bit for bit.  Synchronising the
+// stream after every launch did not change it; the symmetric products, which
+// read no operand through transposing reads, repeat exactly at two per CU.
 template <int BM, int BN, bool LAST, bool XTERM, bool UPD = false>
 __global__ __launch_bounds__((GemmT<BM, BN>::NT), 1) void k_combine_bf16(StepArgs a, const Tile* __restrict__ tiles, int ntiles,
                                                       int src_x, int dst_x, int first, Coeffs cf) {
   constexpr bool last = LAST;
   using G = GemmT<BM, BN>;
   using C = CombT<BM, BN>;
+  constexpr int NB = (BM == 128 && BN == 128) ? 4 : 2;
+  static_assert(NB == 2 || 4 * C::RB * 2 <= 163840, "LDS budget");
   __shared__ __attribute__((aligned(16))) uint16_t ring0[C::RB];
   __shared__ __attribute__((aligned(16))) uint16_t ring1[C::RB];
+  __shared__ __attribute__((aligned(16))) uint16_t ring2[NB == 4 ? C::RB : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t ring3[NB == 4 ? C::RB : 8];
   const Tile t = tiles[xcd_remap(blockIdx.x, ntiles)];
   const MatDesc& d = a.desc[t.mat];
   const uint16_t* Bm = reinterpret_cast<const uint16_t*>(a.ws + d.b_off);
@@ -677,7 +691,10 @@ __global__ __launch_bounds__((GemmT<BM, BN>::NT), 1) void k_combine_bf16(StepArg
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[s][u][r] = 0.0f;
   // B X, with X read k-major: its rows are the product's k.
-  if constexpr (!XTERM) mma_bf16<BM, BN, true>(Bm + gi0 * d.KP, d.KP, X + gj0, d.NP, d.KP, ring0, ring1, acc);
+  if constexpr (!XTERM && NB == 4)
+    mma_bf16<BM, BN, true, false, 0, 4>(Bm + gi0 * d.KP, d.KP, X + gj0, d.NP, d.KP, ring0, ring1, acc, false, ring2, ring3);
+  else if constexpr (!XTERM)
+    mma_bf16<BM, BN, true>(Bm + gi0 * d.KP, d.KP, X + gj0, d.NP, d.KP, ring0, ring1, acc);
 
   const float alpha = first ? a.scal[d.scal_idx].inv_nu : 1.0f;
   const bool partials = LAST && a.dimuon;
@@ -996,8 +1013,8 @@ __global__ __launch_bounds__((GemmT<FT, FT>::NT), 1) void k_combine_f32(StepArgs
 // has CUs (a partial round split off a big-tile list, or a small batch) runs
 // one workgroup per CU anyway, so it takes the deep ring: on the 8 x 4096^2
 // set those launches went from 47.6 to about 41.6 us (Gram and polynomial
-// about 1% faster per step, bit-identical results).  The combine's tail
-// lists measured no faster with it and keep the two-buffer ring.
+// about 1% faster per step, bit-identical results).  The 128 x 128 combine
+// always runs it (see k_combine_bf16).
 // ---------------------------------------------------------------------------
 constexpr int kDeepMaxTiles = 256;
 hipError_t launch_syrk(const StepArgs& a, const Tile* tiles, int n, int bt, int kind, int src_x, bool first,

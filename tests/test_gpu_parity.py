@@ -445,6 +445,29 @@ def test_round_interleave_bit_identical(variant):
 
 
 @pytest.mark.parametrize("variant", ["muon", "dimuon"])
+def test_repeated_steps_bit_identical(variant):
+    # The same step on the same inputs gives the same bits every time.  The
+    # 8 x 1024^2 batch runs its combine on 512 tiles of 128 x 128 (the planner
+    # prefers them to 128 tiles of 256 x 256): with two such workgroups per
+    # CU this once differed between runs in about a thousand elements of X'.
+    shapes = [(1024, 1024)] * 8
+    wl = W.random_batch(shapes, dtype="bf16", ns_dtype="bf16", seed=47, variant=variant)
+    cfg = cfg_of(wl)
+    fn = D.dimuon_step if variant == "dimuon" else D.muon_step
+    announce(f"repeated steps {variant}")
+    runs = []
+    for _ in range(3):
+        ps = _batch_params(wl, range(wl.count))
+        fn(ps, cfg)
+        torch.cuda.synchronize()
+        runs.append([(p.w.float().cpu().numpy(), p.mom.float().cpu().numpy(), p.o_out.cpu().numpy()) for p in ps])
+    for r in runs[1:]:
+        for i in range(wl.count):
+            for k, name in enumerate(("w", "mom", "o_out")):
+                np.testing.assert_array_equal(r[i][k], runs[0][i][k], err_msg=f"matrix {i} {name}")
+
+
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
 def test_symmetric_ring_depths_bit_identical(variant):
     # 8 x 1024^2: the symmetric products run 128 x 128 tiles, 36 per matrix.
     # The batch's 288 tiles exceed one per CU and take the two-buffer ring; a
