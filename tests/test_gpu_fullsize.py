@@ -119,3 +119,28 @@ def test_fullsize_fp32_products(variant):
         for i in range(wl.count):
             announce(f"oracle on matrix {i} {wl.mats[i].shape}")
             check_matrix(gpu, run_oracle(wl, variant, cfg, i), i, cfg, variant, wl)
+
+
+@pytest.mark.parametrize("name", ["lora", "gpt2", "square", "moe"])
+def test_fullsize_plan_steps_repeatable(name):
+    # A plan step over the full benchmark batch, run twice from the same
+    # inputs, gives the same W and M bit for bit (every matrix; compared on
+    # the device).
+    wl, variant = {"lora": lambda: (W.lora_batch(device="cuda"), "dimuon"),
+                   "gpt2": lambda: (W.gpt2_hidden(device="cuda"), "muon"),
+                   "square": lambda: (square_inputs(), "dimuon"),
+                   "moe": lambda: (W.moe_experts(device="cuda"), "dimuon")}[name]()
+    cfg = D.StepConfig(lr=wl.lr, momentum=wl.mu, ns_steps=wl.ns_steps, w_dtype=wl.w_dtype,
+                       g_dtype=wl.g_dtype, mom_dtype=wl.mom_dtype, ns_dtype=wl.ns_dtype)
+    announce(f"{wl.name} {variant}: two plan steps from the same inputs")
+    runs = []
+    for _ in range(2):
+        params = [D.Param(w=m.w.clone(), g=m.g.clone(), mom=m.m_prev.clone()) for m in wl.mats]
+        plan = D.Plan(params, cfg, dimuon=(variant == "dimuon"))
+        plan.step()
+        torch.cuda.synchronize()
+        plan.close()
+        runs.append(params)
+    for i, (a, b) in enumerate(zip(*runs)):
+        assert torch.equal(a.w, b.w), f"matrix {i}: W differs between identical steps"
+        assert torch.equal(a.mom, b.mom), f"matrix {i}: M differs between identical steps"
