@@ -37,9 +37,9 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 # profiles/k_thin_lora_batch_64x8x4096.md.
 THIN_SOURCES = ("dimuon_newton_schulz_amd/csrc/thin_kernel.hip", "dimuon_newton_schulz_amd/csrc/common.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "963df4ed03f6ab9e3a50a75e63f078ecf1b8a4a7e0eedf695dd12c7844a8b934",
-    "k_thin_a": {"fetch_kib": 18130.1, "write_kib": 19012.9},
-    "k_thin_b": {"fetch_kib": 20388.1, "write_kib": 18496.0},
+    "sources_sha256": "160946e9c2ddb41ea3516b022b0800165d01f90a7fb49da8cf6678f5ec90f4a3",
+    "k_thin_a": {"fetch_kib": 17684.7, "write_kib": 19012.0},
+    "k_thin_b": {"fetch_kib": 18036.1, "write_kib": 18468.0},
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 

@@ -519,10 +519,20 @@ __device__ __forceinline__ void energy_body(const StepArgs& args, const MatDesc&
   energies_to_cache<KP>(y, d, s, l0, cache_of(args, d, parity), sm);
 }
 
+// Workgroups are dealt round-robin to the 8 XCDs; each XCD takes a
+// contiguous run of the slice list instead, so that the slices of a matrix
+// share an L2 (pass B's workgroups each read every slice's Gram partials of
+// their matrix, pass A's the matrix's cached row energies).
+__device__ __forceinline__ int slice_of_block() {
+  const int n = static_cast<int>(gridDim.x), bid = static_cast<int>(blockIdx.x);
+  const int q = n >> 3, r = n & 7, xcd = bid & 7, idx = bid >> 3;
+  return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
+}
+
 template <int KP>
 __global__ __launch_bounds__(TT) void k_thin_energy(StepArgs args, const Tile* __restrict__ tiles, int parity) {
   __shared__ ThinSmem<KP> sm;
-  const Tile t = tiles[blockIdx.x];
+  const Tile t = tiles[slice_of_block()];
   const MatDesc& d = args.desc[t.mat];
   if (d.tall) energy_body<KP, true>(args, d, t.ti, parity, sm);
   else energy_body<KP, false>(args, d, t.ti, parity, sm);
@@ -642,7 +652,7 @@ template <int KP, typename TA, bool MFG>
 __global__ __launch_bounds__(TT, 4) void k_thin_a(StepArgs args, const Tile* __restrict__ tiles, int parity) {
   static_assert(!MFG || (sizeof(TA) == 4 && gram_on_mfma<KP>()), "matrix-core Gram: bf16 mode, Gram side 8");
   __shared__ ThinSmem<KP> sm;
-  const Tile t = tiles[blockIdx.x];
+  const Tile t = tiles[slice_of_block()];
   const MatDesc& d = args.desc[t.mat];
   if (d.tall) pass_a_body<KP, true, TA, MFG>(args, d, t.ti, parity, sm);
   else pass_a_body<KP, false, TA, MFG>(args, d, t.ti, parity, sm);
@@ -964,7 +974,7 @@ template <int KP>
 __global__ __launch_bounds__(TT) void k_thin_b(StepArgs args, const Tile* __restrict__ tiles, int ns_steps,
                                                 ThinCoeffs cf, int parity) {
   __shared__ ThinSmem<KP> sm;
-  const Tile t = tiles[blockIdx.x];
+  const Tile t = tiles[slice_of_block()];
   const MatDesc& d = args.desc[t.mat];
   if (d.tall) pass_b_body<KP, true>(args, d, t.ti, ns_steps, cf, parity, sm);
   else pass_b_body<KP, false>(args, d, t.ti, ns_steps, cf, parity, sm);
