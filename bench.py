@@ -54,13 +54,13 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 GEMM_SOURCES = ("dimuon_newton_schulz_amd/csrc/gemm_kernels.hip", "dimuon_newton_schulz_amd/csrc/api.hip",
                 "dimuon_newton_schulz_amd/csrc/common.h")
 MEASURED_GEMM = {
-    "sources_sha256": "d983aa282dfa579b58bb688d27c63d4496135faa1953d86682a61a561c3b323e",
-    "gpt2_small_12x4_bf16": {"fetch_kib": [134463.6, 5270.3], "write_kib": [163840.0, 2048.0],
-                             "mfma_busy_frac": 0.361, "clock_ghz": 2.19},
-    "square_8x4096x4096_bf16": {"fetch_kib": [786611.0], "write_kib": [262237.8],
-                                "mfma_busy_frac": 0.572, "clock_ghz": 1.94},
-    "moe_64x(2048x1408+1408x2048)_bf16": {"fetch_kib": [963599.3], "write_kib": [786441.6],
-                                          "mfma_busy_frac": 0.473, "clock_ghz": 1.94},
+    "sources_sha256": "3581e9c0f312ee0b2ed9ff96fd0acfd670c9b27cba6d628182b686e5a251f1ff",
+    "gpt2_small_12x4_bf16": {"fetch_kib": [134273.6, 5270.3], "write_kib": [163840.1, 2048.0],
+                             "mfma_busy_frac": 0.363, "clock_ghz": 2.17},
+    "square_8x4096x4096_bf16": {"fetch_kib": [786652.0], "write_kib": [262231.2],
+                                "mfma_busy_frac": 0.573, "clock_ghz": 1.94},
+    "moe_64x(2048x1408+1408x2048)_bf16": {"fetch_kib": [968372.0], "write_kib": [786466.5],
+                                          "mfma_busy_frac": 0.475, "clock_ghz": 1.92},
 }
 
 

@@ -657,15 +657,20 @@ __global__ __launch_bounds__((GemmT<BT, BT, kSyrkWC<BT>>::NT), 1) void k_syrk_bf
 // XTERM (no iterations: Z = alpha a X): the product is skipped and X read.
 // ---------------------------------------------------------------------------
 //
-// 128 x 128 tiles run the four-buffer ring (four separate arrays, so that
-// the compiler can tell the stages apart), which also makes them run one
-// workgroup per CU.  Two workgroups of the two-buffer 128 x 128 combine on
-// one CU gave results that differed between identical runs (about a
-// thousand elements of X' per launch of 512 tiles, 8 x 1024^2, while its
-// inputs were the same bit for bit); with one workgroup per CU, or with the
-// four-buffer ring, repeated runs agree bit for bit.  Synchronising the
-// stream after every launch did not change it; the symmetric products, which
-// read no operand through transposing reads, repeat exactly at two per CU.
+// Every combine workgroup holds the whole 160 KB of a CU's LDS, so no other
+// workgroup that uses LDS runs beside it.  Transposing LDS reads of one
+// workgroup overlapping another workgroup's LDS staging on the same CU gave
+// results that differed between identical runs: with two workgroups of the
+// 128 x 128 combine per CU, about a thousand elements of X' per launch of
+// 512 tiles (8 x 1024^2) while its inputs were the same bit for bit.  Probe
+// copies of the kernel, two workgroups per CU, repeat exactly with the main
+// loop alone, with the epilogue alone, with an 800 us pause between the two
+// phases, and with plain 16-byte reads of both operands in the main loop;
+// they differ in every repeat only when the transposing reads of one
+// workgroup meet the other's epilogue.  Every LDS address of both phases lies
+// inside the workgroup's own arrays.  The 128 x 128 tiles also run the
+// four-buffer ring (four separate arrays, so that the compiler can tell the
+// stages apart).
 template <int BM, int BN, bool LAST, bool XTERM, bool UPD = false>
 __global__ __launch_bounds__((GemmT<BM, BN>::NT), 1) void k_combine_bf16(StepArgs a, const Tile* __restrict__ tiles, int ntiles,
                                                       int src_x, int dst_x, int first, Coeffs cf) {
@@ -678,6 +683,10 @@ __global__ __launch_bounds__((GemmT<BM, BN>::NT), 1) void k_combine_bf16(StepArg
   __shared__ __attribute__((aligned(16))) uint16_t ring1[C::RB];
   __shared__ __attribute__((aligned(16))) uint16_t ring2[NB == 4 ? C::RB : 8];
   __shared__ __attribute__((aligned(16))) uint16_t ring3[NB == 4 ? C::RB : 8];
+  // The rest of the CU's LDS (the factor array below included; 64 bytes
+  // left for alignment).
+  constexpr int kUsed = (NB == 4 ? 4 * C::RB : 2 * C::RB + 16) * 2 + (LAST ? BM + BN : 1) * 4;
+  __shared__ __attribute__((aligned(16))) volatile uint32_t lds_rest[(163840 - 64 - kUsed) / 4];
   const Tile t = tiles[xcd_remap(blockIdx.x, ntiles)];
   const MatDesc& d = a.desc[t.mat];
   const uint16_t* Bm = reinterpret_cast<const uint16_t*>(a.ws + d.b_off);
@@ -838,6 +847,7 @@ __global__ __launch_bounds__((GemmT<BM, BN>::NT), 1) void k_combine_bf16(StepArg
       }
     }
   }
+  if (ntiles < 0) lds_rest[0] = 0u;   // never taken; keeps lds_rest allocated
 }
 
 // ---------------------------------------------------------------------------
