@@ -468,6 +468,40 @@ def test_repeated_steps_bit_identical(variant):
 
 
 @pytest.mark.parametrize("variant", ["muon", "dimuon"])
+def test_two_plans_on_two_streams_match_one_plan(variant):
+    # A batch split into two plans stepped on two streams (their kernels may
+    # then share CUs) gives what one plan over the whole batch gives, bit for
+    # bit.  8 x 1024^2 runs 128 x 128 combine tiles, GPT-2 shapes 256 x 256.
+    for wl in (W.random_batch([(1024, 1024)] * 8, dtype="bf16", ns_dtype="bf16", seed=49, variant=variant),
+               W.gpt2_hidden(layers=4, seed=1, device="cuda")):
+        cfg = cfg_of(wl)
+        dimuon = variant == "dimuon"
+        announce(f"two plans on two streams {variant} {wl.name}")
+        one = _batch_params(wl, range(wl.count))
+        plan = D.Plan(one, cfg, dimuon)
+        plan.step()
+        torch.cuda.synchronize()
+        plan.close()
+        two = _batch_params(wl, range(wl.count))
+        p0, p1 = D.Plan(two[0::2], cfg, dimuon), D.Plan(two[1::2], cfg, dimuon)
+        main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+        fork = torch.cuda.Event()
+        fork.record(main)
+        side.wait_event(fork)
+        p0.step(main)
+        p1.step(side)
+        join = torch.cuda.Event()
+        join.record(side)
+        main.wait_event(join)
+        torch.cuda.synchronize()
+        p0.close()
+        p1.close()
+        for i, (a, b) in enumerate(zip(one, two)):
+            for name in ("w", "mom", "o_out"):
+                assert torch.equal(getattr(a, name), getattr(b, name)), f"{wl.name} matrix {i} {name}"
+
+
+@pytest.mark.parametrize("variant", ["muon", "dimuon"])
 def test_symmetric_ring_depths_bit_identical(variant):
     # 8 x 1024^2: the symmetric products run 128 x 128 tiles, 36 per matrix.
     # The batch's 288 tiles exceed one per CU and take the two-buffer ring; a
