@@ -37,7 +37,7 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 # profiles/k_thin_lora_batch_64x8x4096.md.
 THIN_SOURCES = ("dimuon_newton_schulz_amd/csrc/thin_kernel.hip", "dimuon_newton_schulz_amd/csrc/common.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "160946e9c2ddb41ea3516b022b0800165d01f90a7fb49da8cf6678f5ec90f4a3",
+    "sources_sha256": "e35e3c4802044f21fb56a03786e5766071f0f5d903b32c8d9217c7ef0e710aeb",
     "k_thin_a": {"fetch_kib": 17684.7, "write_kib": 19012.0},
     "k_thin_b": {"fetch_kib": 18036.1, "write_kib": 18468.0},
 }
@@ -54,7 +54,7 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 GEMM_SOURCES = ("dimuon_newton_schulz_amd/csrc/gemm_kernels.hip", "dimuon_newton_schulz_amd/csrc/api.hip",
                 "dimuon_newton_schulz_amd/csrc/common.h")
 MEASURED_GEMM = {
-    "sources_sha256": "3581e9c0f312ee0b2ed9ff96fd0acfd670c9b27cba6d628182b686e5a251f1ff",
+    "sources_sha256": "cf7e0845c718b4c011d8f77514d35717d007443866948b486c52999ccee92a78",
     "gpt2_small_12x4_bf16": {"fetch_kib": [134273.6, 5270.3], "write_kib": [163840.1, 2048.0],
                              "mfma_busy_frac": 0.363, "clock_ghz": 2.17},
     "square_8x4096x4096_bf16": {"fetch_kib": [786652.0], "write_kib": [262231.2],

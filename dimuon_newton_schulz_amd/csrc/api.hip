@@ -93,7 +93,8 @@ struct Plan {
 };
 
 // Thin path: Gram side k <= 32.  Each slice of the long side is one
-// 256-thread workgroup holding 32 values per thread, i.e. 8192 / KP positions.
+// 256-thread workgroup holding max(16, KP) values per thread and array, i.e.
+// 256 * max(16, KP) / KP positions (thin_slice_len).
 bool is_thin(int64_t m, int64_t n) { return std::min(m, n) <= kThinMaxK; }
 
 muon_status_t validate_config(const muon_config_t* cfg) {

@@ -12,14 +12,17 @@
 // kernels at the end of this file keep X^T beside X and stay "NT".
 //
 // bf16 path: a BM x BN workgroup tile (BM, BN in {128, 256}), wave64s in a
-// 2 x WC grid (eight waves, WC = 4, for the larger tiles; four for 128 x 128),
-// each wave owning (BM/2) x (BN/WC) as 32 x 32 blocks of
-// v_mfma_f32_32x32x16_bf16.  Operands go from global memory straight into a
-// ring of two LDS stages of 64 k-values (global_load_lds_dwordx4, no register
-// staging); one stage is in flight while the other is multiplied (the loop
-// is pipelined so that LDS fragment reads are covered by MFMAs).  A 256 x 256
-// tile needs half the L2 traffic per flop of a 128 x 128 one; with its 128 KB
-// ring one workgroup runs per CU (two for 128 x 128).
+// 2 x WC grid, each wave owning (BM/2) x (BN/WC) as 32 x 32 blocks of
+// v_mfma_f32_32x32x16_bf16 (wave counts per kernel below).  Operands go from
+// global memory straight into a ring of LDS stages of 64 k-values
+// (global_load_lds_dwordx4, no register staging): two stages, one in flight
+// while the other is multiplied, or four (up to three in flight) where a
+// 128 x 128 workgroup has a CU's LDS to itself.  The loop is pipelined so
+// that LDS fragment reads are covered by MFMAs.  A 256 x 256 tile needs half
+// the L2 traffic per flop of a 128 x 128 one; with its 128 KB ring one
+// workgroup runs per CU.  The 128 x 128 symmetric products run two per CU
+// (one per CU, on the four-stage ring, for lists no longer than the GPU has
+// CUs); every combine workgroup holds a whole CU's LDS.
 //
 // The epilogue stages the fp32 accumulators through LDS (transposed, in
 // rounds) so that the row-major and the transposed outputs are written as
@@ -38,15 +41,16 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int LBK = 64;        // k per pipeline stage: whole 128-byte lines of each operand row
 constexpr int NQ = LBK / 16;   // MFMA k-steps per stage
 
-// The ring holds two stages of 64 k (128 KB for 256 x 256, 96 KB for
-// 128 x 256, 64 KB for 128 x 128, which runs two workgroups per CU); one is
-// multiplied while the next is in flight.  Whole-line stages fetch faster
-// than half-line ones (each row's 128 bytes arrive as one request), and a
-// deeper ring of shorter stages measured no faster.
-// Waves in 2 rows x WC columns.  Tiles of 128 x 256 and larger run eight
-// waves (WC = 4, two per SIMD: one wave's MFMAs cover the other's loads and
-// barrier waits), measured 3-5% faster per step than four; 128 x 128 tiles,
-// two workgroups per CU, keep four (eight measured slower there).
+// The two-stage ring takes 128 KB for 256 x 256, 96 KB for 128 x 256 and
+// 64 KB for 128 x 128; one stage is multiplied while the next is in flight.
+// Whole-line stages fetch faster than half-line ones (each row's 128 bytes
+// arrive as one request), and a deeper ring of shorter stages measured no
+// faster.
+// Waves in 2 rows x WC columns.  By this rule tiles of 128 x 256 and larger
+// run eight waves (WC = 4, two per SIMD: one wave's MFMAs cover the other's
+// loads and barrier waits), measured 3-5% faster per step than four, and
+// 128 x 128 tiles four (eight measured slower there); the 256 x 256
+// symmetric products set four waves apart from the rule (kSyrkWC).
 #ifndef MUON_GEMM_WC_LARGE
 #define MUON_GEMM_WC_LARGE 4
 #endif

@@ -5,7 +5,8 @@
 // positions, and one 256-thread workgroup handles one slice.  Thread t of
 // slice s owns VEC consecutive positions s*L + t*VEC .. +VEC-1 and all KP
 // Gram-side rows of them (KP = k rounded up to a power of two,
-// KP * VEC = 32), so every thread holds 32 values per array.
+// KP * VEC = max(16, KP)), so every thread holds 16 values per array up to
+// Gram side 16 and 32 at Gram side 32.
 //
 // Newton-Schulz in Gram space: with X_0 = Y / ||Y||_F and A_0 = X_0 X_0^T,
 // every iterate of X <- aX + b(XX^T)X + c(XX^T)^2 X = (aI + bA + cA^2) X
